@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the QK4PV8 attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = the whole prefill hot path over the Llama-3.1-8B-shaped workload
+(B1, Hq32/Hkv8, S16384, D128, causal; bf16 inputs resident in HBM): quantise Q
+and K to MXFP4, V to FP8, and run the fused prefill kernel.  `value` is
+algorithmic TFLOP/s of the whole step (4 D FLOPs per visible query/key pair;
+masked pairs not counted).  The decode half of the metric (B64 sequences x
+32768 cached keys, Hq32/Hkv8, 16 KV splits + LSE merge, cache pre-quantised)
+is timed in the same run and reported under "decode" as KV GB/s.
+
+The roofline object is for the dominant kernel (the prefill kernel), timed
+with HIP events on the stream it is launched on; its peak is the blended
+MXFP4 (Q K^T) / FP8 (P V) MFMA peak.  The CPU baseline is the oracle timed on
+a bounded sample of rows of the same workload on this host.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--workload", default="llama16k")
+    return p.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("attn.hip", "quant.hip", "api.hip", "qfa_internal.h"):
+        with open(os.path.join(ROOT, "bit_quantized_attention_qk4pv8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(name, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each GPU would run its own shard with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_attention_qk4pv8_amd as qfa
+    from bit_quantized_attention_qk4pv8_amd import roofline as rl
+    from bit_quantized_attention_qk4pv8_amd.workloads import WORKLOADS, bf16_bits, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w, seed=0, device=dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    B, Hq, Hkv, S, D = w.B, w.Hq, w.Hkv, w.S_q, w.D
+    nt = (S + 127) // 128
+    q4 = torch.empty((B, Hq, S, D // 2), dtype=torch.uint8, device=dev)
+    q4s = torch.empty((B, Hq, S, D // 32), dtype=torch.uint8, device=dev)
+    k4 = torch.empty((B, Hkv, S, D // 2), dtype=torch.uint8, device=dev)
+    k4s = torch.empty((B, Hkv, S, D // 32), dtype=torch.uint8, device=dev)
+    kbar = torch.empty((B, Hkv, nt, D), dtype=torch.bfloat16, device=dev) if w.smooth else None
+    v8 = torch.empty((B, Hkv, (S + 31) // 32, D, 32), dtype=torch.uint8, device=dev)
+    v8s = torch.empty((B, Hkv, (S + 31) // 32, D), dtype=torch.uint8, device=dev)
+    O = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i=None):
+        qfa.qfa_quantize_qk4(q, B, Hq, S, D, 32, 0, q4, q4s, None, stream)
+        qfa.qfa_quantize_qk4(k, B, Hkv, S, D, 32, int(w.smooth), k4, k4s, kbar, stream)
+        qfa.qfa_quantize_v8(v, B, Hkv, S, D, 32, v8, v8s, stream)
+        if i is not None:
+            ev[i][0].record(stream)
+        qfa.qfa_fwd_prefill(q4, q4s, k4, k4s, kbar, q if w.smooth else None, v8, v8s, B, Hq, Hkv, S, S, D,
+                            int(w.causal), w.scale, 32, O, lse, stream)
+        if i is not None:
+            ev[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = w.flops()
+    comp = w.comp_flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = (flops + comp) / (kern_ms * 1e-3) / 1e12
+    peak = rl.blended_peak(flops, comp) / 1e12
+    src = source_hash()
+    traffic = traffic_from_profile("prefill_%s_traffic.json" % w.name, src)
+    out = {
+        "metric": "QK4PV8 fwd prefill TFLOP/s (+ decode KV GB/s) on 1xMI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4(QK)+fp8(PV), fp32 accumulate",
+        "data": "synthetic seeded bf16 inputs shaped like Llama-3.1-8B attention (no weights/datasets)",
+        "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "S_q": S, "S_kv": S, "D": D,
+                   "causal": w.causal, "compensation": w.smooth,
+                   "step": "quantize Q,K (MXFP4) + V (FP8) + fused prefill"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 2), "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "qfa::k_prefill<128,%s>" % ("true" if w.smooth else "false"),
+                     "kernel_ms": round(kern_ms, 4), "algorithmic_flop_per_launch": flops + comp},
+    }
+    del O, lse
+    # ------------------------------------------------------------------ decode half
+    if not args.no_decode:
+        wd = WORKLOADS["decode"]
+        di = make_inputs(wd, seed=0, device=dev)
+        Bd, Hqd, Hkvd, L, Dd = di["B"], wd.Hq, wd.Hkv, wd.S_kv, wd.D
+        k4d, k4sd, _ = qfa.quantize_qk4(di["k"])
+        v8d, v8sd = qfa.quantize_v8(di["v"])
+        qd = di["q"]
+        del di
+        q4d = torch.empty((Bd, Hqd, 1, Dd // 2), dtype=torch.uint8, device=dev)
+        q4sd = torch.empty((Bd, Hqd, 1, Dd // 32), dtype=torch.uint8, device=dev)
+        splits = wd.num_splits
+        wsb = qfa.qfa_decode_workspace_bytes(Bd, Hqd, Dd, splits)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        Od = torch.empty((Bd, Hqd, Dd), dtype=torch.float32, device=dev)
+        lsed = torch.empty((Bd, Hqd), dtype=torch.float32, device=dev)
+        dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+
+        def dstep(i=None):
+            qfa.qfa_quantize_qk4(qd, Bd, Hqd, 1, Dd, 32, 0, q4d, q4sd, None, stream)
+            if i is not None:
+                dev_ev[i][0].record(stream)
+            qfa.qfa_fwd_decode(q4d, q4sd, k4d, k4sd, None, None, v8d, v8sd, Bd, Hqd, Hkvd, L, None, Dd, wd.scale,
+                               32, splits, ws, wsb, Od, lsed, stream)
+            if i is not None:
+                dev_ev[i][1].record(stream)
+
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            dstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            dstep(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        d_ms = (t1 - t0) * 1e3 / args.steps
+        d_kern = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+        dbytes = rl.decode_algorithmic_bytes(Bd, Hqd, Hkvd, L, Dd)
+        gbs = dbytes / (d_kern * 1e-3) / 1e9
+        out["decode"] = {
+            "metric": "decode KV GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_step": round(d_ms, 4), "kernel_ms": round(d_kern, 4),
+            "config": {"workload": "decode", "B": Bd, "Hq": Hqd, "Hkv": Hkvd, "S_kv": L, "D": Dd,
+                       "num_splits": splits},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": rl.PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": round(gbs * 1e9 / rl.PEAK_HBM, 4),
+                         "traffic": traffic_from_profile("decode_b64_traffic.json", src),
+                         "kernel": "qfa::k_decode_split<128,false> + k_decode_merge<128>",
+                         "algorithmic_bytes_per_launch": dbytes},
+        }
+        del k4d, v8d, ws
+    # ------------------------------------------------------------------ CPU baseline (oracle)
+    if not args.no_cpu_baseline:
+        import oracle
+        qb = bf16_bits(q)
+        kb = bf16_bits(k)
+        vb = bf16_bits(v)
+        rng = np.random.default_rng(0)
+        # a bounded sample: whole query heads cost too much; take rows spread over positions
+        n_rows = 48
+        rows = np.stack([np.zeros(n_rows, np.int64), rng.integers(0, Hq, n_rows),
+                         rng.integers(0, S, n_rows)], axis=1)
+        tc0 = time.perf_counter()
+        oracle.prefill_rows(qb, kb, vb, rows, w.causal, w.scale, smooth=w.smooth, exact=False)
+        tc1 = time.perf_counter()
+        sample_pairs = int(sum((r[2] + 1) if w.causal else S for r in rows))
+        cpu_tflops = 4.0 * D * sample_pairs / (tc1 - tc0) / 1e12
+        out["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": "%d random query rows of %s (all their visible keys), including "
+                                         "quantising the K/V heads and Q heads they touch; %.1f s" %
+                                         (n_rows, w.name, tc1 - tc0)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+"""Python binding of libqfa, the QK4PV8 attention forward library for MI355X.
+
+Every function named ``qfa_*`` mirrors the C entry point of the same name in
+``include/qfa.h``: it only marshals torch tensors (device memory) and the
+current HIP stream into the call, and raises ``QfaError`` on a non-OK status.
+All arithmetic runs in the HIP kernels of ``libqfa.so``; there is no fallback
+path -- if the library is not built, importing works but the first call raises.
+
+The ``quantize_*`` / ``fwd_*`` helpers allocate the outputs with torch and call
+the ``qfa_*`` functions.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqfa.so")
+
+QFA_OK = 0
+QFA_ERR_INVALID_ARG = 1
+QFA_ERR_UNSUPPORTED = 2
+QFA_ERR_WORKSPACE = 3
+QFA_ERR_HIP = 4
+
+EXPORTS = (
+    "qfa_quantize_qk4", "qfa_quantize_v8", "qfa_fwd_prefill", "qfa_fwd_decode",
+    "qfa_decode_workspace_bytes", "qfa_decode_default_splits", "qfa_status_string", "qfa_version",
+)
+
+_lib = None
+
+
+class QfaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s" % (fn, status_string(status)))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqfa.so (built in-tree by ``python -m bit_quantized_attention_qk4pv8_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libqfa.so is not built; run `python -m bit_quantized_attention_qk4pv8_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.qfa_quantize_qk4.restype = I
+        L.qfa_quantize_qk4.argtypes = [P, I, I, I, I, I, I, P, P, P, P]
+        L.qfa_quantize_v8.restype = I
+        L.qfa_quantize_v8.argtypes = [P, I, I, I, I, I, P, P, P]
+        L.qfa_fwd_prefill.restype = I
+        L.qfa_fwd_prefill.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, P, P]
+        L.qfa_fwd_decode.restype = I
+        L.qfa_fwd_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P, I, F, I, ctypes.POINTER(I), P, SZ, P,
+                                     P, P]
+        L.qfa_decode_workspace_bytes.restype = SZ
+        L.qfa_decode_workspace_bytes.argtypes = [I, I, I, I]
+        L.qfa_decode_default_splits.restype = I
+        L.qfa_decode_default_splits.argtypes = [I, I, I]
+        L.qfa_status_string.restype = ctypes.c_char_p
+        L.qfa_status_string.argtypes = [I]
+        L.qfa_version.restype = I
+        L.qfa_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qfa_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libqfa must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != QFA_OK:
+        raise QfaError(fn, status)
+
+
+def _u16(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+# ----------------------------------------------------------------------------- C entry points
+def qfa_version() -> int:
+    return lib().qfa_version()
+
+
+def qfa_decode_workspace_bytes(B: int, Hq: int, D: int, num_splits: int) -> int:
+    return lib().qfa_decode_workspace_bytes(B, Hq, D, num_splits)
+
+
+def qfa_decode_default_splits(B: int, Hkv: int, S_kv_max: int) -> int:
+    return lib().qfa_decode_default_splits(B, Hkv, S_kv_max)
+
+
+def qfa_quantize_qk4(x, B, H, S, D, block_size, smooth, codes, scales, kbar, stream=None):
+    _check("qfa_quantize_qk4", lib().qfa_quantize_qk4(_ptr(_u16(x)), B, H, S, D, block_size, int(smooth),
+                                                      _ptr(codes), _ptr(scales), _ptr(kbar), _stream(stream)))
+
+
+def qfa_quantize_v8(v, B, H, S, D, block_size, codes, scales, stream=None):
+    _check("qfa_quantize_v8", lib().qfa_quantize_v8(_ptr(_u16(v)), B, H, S, D, block_size, _ptr(codes),
+                                                    _ptr(scales), _stream(stream)))
+
+
+def qfa_fwd_prefill(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_q, S_kv, D, causal, softmax_scale,
+                    block_size, O, lse, stream=None):
+    _check("qfa_fwd_prefill", lib().qfa_fwd_prefill(
+        _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(None if kbar is None else _u16(kbar)),
+        _ptr(None if q_bf16 is None else _u16(q_bf16)), _ptr(v8), _ptr(v8s), B, Hq, Hkv, S_q, S_kv, D,
+        int(causal), float(softmax_scale), block_size, _ptr(O), _ptr(lse), _stream(stream)))
+
+
+def qfa_fwd_decode(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D, softmax_scale,
+                   block_size, num_splits, workspace, workspace_bytes, O, lse, stream=None) -> int:
+    ns = ctypes.c_int(int(num_splits))
+    _check("qfa_fwd_decode", lib().qfa_fwd_decode(
+        _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(None if kbar is None else _u16(kbar)),
+        _ptr(None if q_bf16 is None else _u16(q_bf16)), _ptr(v8), _ptr(v8s), B, Hq, Hkv, S_kv_max,
+        _ptr(kv_lens), D, float(softmax_scale), block_size, ctypes.byref(ns), _ptr(workspace),
+        int(workspace_bytes), _ptr(O), _ptr(lse), _stream(stream)))
+    return ns.value
+
+
+# ----------------------------------------------------------------------------- allocating helpers
+def quantize_qk4(x: torch.Tensor, smooth: bool = False, stream=None):
+    """x bf16 [B,H,S,D] on the GPU -> (codes u8 [B,H,S,D/2], scales u8 [B,H,S,D/32], kbar bf16 or None)."""
+    B, H, S, D = x.shape
+    codes = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H, S, D // 32), dtype=torch.uint8, device=x.device)
+    kbar = torch.empty((B, H, (S + 127) // 128, D), dtype=torch.bfloat16, device=x.device) if smooth else None
+    qfa_quantize_qk4(x, B, H, S, D, 32, smooth, codes, scales, kbar, stream)
+    return codes, scales, kbar
+
+
+def quantize_v8(v: torch.Tensor, stream=None):
+    """v bf16 [B,H,S,D] -> (codes u8 [B,H,ceil(S/32),D,32], scales u8 [B,H,ceil(S/32),D])."""
+    B, H, S, D = v.shape
+    nb = (S + 31) // 32
+    codes = torch.empty((B, H, nb, D, 32), dtype=torch.uint8, device=v.device)
+    scales = torch.empty((B, H, nb, D), dtype=torch.uint8, device=v.device)
+    qfa_quantize_v8(v, B, H, S, D, 32, codes, scales, stream)
+    return codes, scales
+
+
+def fwd_prefill(q4, q4s, k4, k4s, v8, v8s, S_kv: int, causal: bool, softmax_scale: float, kbar=None,
+                q_bf16=None, with_lse: bool = True, stream=None):
+    B, Hq, S_q, Dh = q4.shape
+    D = Dh * 2
+    Hkv = k4.shape[1]
+    O = torch.empty((B, Hq, S_q, D), dtype=torch.float32, device=q4.device)
+    lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=q4.device) if with_lse else None
+    qfa_fwd_prefill(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_q, S_kv, D, causal, softmax_scale, 32,
+                    O, lse, stream)
+    return O, lse
+
+
+def fwd_decode(q4, q4s, k4, k4s, v8, v8s, S_kv_max: int, softmax_scale: float, num_splits: int = 0,
+               kv_lens=None, kbar=None, q_bf16=None, workspace=None, stream=None):
+    """q4 [B,Hq,1,D/2]; returns (O [B,Hq,D], lse [B,Hq], splits used)."""
+    B, Hq, _, Dh = q4.shape
+    D = Dh * 2
+    Hkv = k4.shape[1]
+    splits = num_splits if num_splits > 0 else qfa_decode_default_splits(B, Hkv, S_kv_max)
+    nbytes = qfa_decode_workspace_bytes(B, Hq, D, splits)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q4.device)
+    O = torch.empty((B, Hq, D), dtype=torch.float32, device=q4.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q4.device)
+    used = qfa_fwd_decode(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D,
+                          softmax_scale, 32, splits, workspace, workspace.numel(), O, lse, stream)
+    return O, lse, used

@@ -1,0 +1,158 @@
+// extern "C" entry points of libqfa: argument validation on the host, then
+// kernel launches on the caller's stream.  See include/qfa.h for the contract.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/qfa.h"
+#include "qfa_internal.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool qk_dim_ok(int D) { return D >= 32 && D <= 256 && D % 32 == 0; }
+bool attn_dim_ok(int D) { return D == 64 || D == 128; }
+
+qfa_status from_hip(hipError_t e) { return e == hipSuccess ? QFA_OK : QFA_ERR_HIP; }
+
+// log2(e) rounded to binary32; the kernels form the exponent argument from
+// c2 = fl32(softmax_scale * log2e).
+constexpr float kLog2e = 1.44269502162933349609375f;
+
+size_t ws_bytes(int B, int Hq, int D, int splits) {
+  const size_t rows = (size_t)B * Hq * splits;
+  size_t o = rows * D * sizeof(float);
+  o = (o + 255) / 256 * 256;
+  return o + (rows * sizeof(float) + 255) / 256 * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qfa_status_string(qfa_status status) {
+  switch (status) {
+    case QFA_OK: return "QFA_OK";
+    case QFA_ERR_INVALID_ARG: return "QFA_ERR_INVALID_ARG";
+    case QFA_ERR_UNSUPPORTED: return "QFA_ERR_UNSUPPORTED";
+    case QFA_ERR_WORKSPACE: return "QFA_ERR_WORKSPACE";
+    case QFA_ERR_HIP: return "QFA_ERR_HIP";
+  }
+  return "QFA_ERR_UNKNOWN";
+}
+
+int qfa_version(void) { return kVersion; }
+
+qfa_status qfa_quantize_qk4(const uint16_t* x, int B, int H, int S, int D, int block_size, int smooth,
+                            uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t stream) {
+  if (block_size != 32 || !qk_dim_ok(D)) return QFA_ERR_UNSUPPORTED;
+  if (B < 0 || H < 0 || S < 0 || (long long)B * H > 65535) return QFA_ERR_INVALID_ARG;
+  if (smooth != 0 && smooth != 1) return QFA_ERR_INVALID_ARG;
+  if ((smooth == 1) != (kbar != nullptr)) return QFA_ERR_INVALID_ARG;
+  if ((long long)B * H * S == 0) return QFA_OK;
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return QFA_ERR_INVALID_ARG;
+  if (kbar && !aligned16(kbar)) return QFA_ERR_INVALID_ARG;
+  return from_hip(qfa::launch_quant_qk4(x, B, H, S, D, smooth, codes, scales, kbar, stream));
+}
+
+qfa_status qfa_quantize_v8(const uint16_t* v, int B, int H, int S, int D, int block_size, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream) {
+  if (block_size != 32 || !qk_dim_ok(D)) return QFA_ERR_UNSUPPORTED;
+  if (B < 0 || H < 0 || S < 0 || (long long)B * H > 65535) return QFA_ERR_INVALID_ARG;
+  if ((long long)B * H * S == 0) return QFA_OK;
+  if (!v || !codes || !scales || !aligned16(v) || !aligned16(codes)) return QFA_ERR_INVALID_ARG;
+  return from_hip(qfa::launch_quant_v8(v, B, H, S, D, codes, scales, stream));
+}
+
+static qfa_status check_attn_common(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                                    const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8,
+                                    const uint8_t* v8s, int B, int Hq, int Hkv, int D, float softmax_scale,
+                                    int block_size, const float* O) {
+  if (block_size != 32 || !attn_dim_ok(D)) return QFA_ERR_UNSUPPORTED;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return QFA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return QFA_ERR_INVALID_ARG;
+  if ((kbar == nullptr) != (q_bf16 == nullptr)) return QFA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q4, k4, v8, O};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return QFA_ERR_INVALID_ARG;
+  if (!q4s || !k4s || !v8s) return QFA_ERR_INVALID_ARG;
+  if (kbar && (!aligned16(kbar) || !aligned16(q_bf16))) return QFA_ERR_INVALID_ARG;
+  return QFA_OK;
+}
+
+qfa_status qfa_fwd_prefill(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                           const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                           int B, int Hq, int Hkv, int S_q, int S_kv, int D, int causal, float softmax_scale,
+                           int block_size, float* O, float* lse, hipStream_t stream) {
+  if (S_q < 0 || S_kv < 0 || (causal != 0 && causal != 1)) return QFA_ERR_INVALID_ARG;
+  if ((long long)B * Hq * S_q == 0) return QFA_OK;
+  qfa_status st = check_attn_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, D, softmax_scale,
+                                    block_size, O);
+  if (st != QFA_OK) return st;
+  const long long nq = (S_q + 31) / 32;
+  const int G = Hq / Hkv;
+  const long long nwg = (long long)B * Hkv * ((G + 7) / 8) * nq;
+  if (nwg > 0x7FFFFFFFLL) return QFA_ERR_INVALID_ARG;
+  qfa::AttnArgs a{};
+  a.q4 = q4; a.q4s = q4s; a.k4 = k4; a.k4s = k4s; a.v8 = v8; a.v8s = v8s;
+  a.kbar = kbar; a.qbf = q_bf16; a.kv_lens = nullptr;
+  a.O = O; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = S_q; a.Skv = S_kv; a.D = D; a.G = G;
+  a.causal = causal;
+  a.c2 = softmax_scale * kLog2e;
+  a.num_splits = 1;
+  return from_hip(qfa::launch_prefill(a, stream));
+}
+
+int qfa_decode_default_splits(int B, int Hkv, int S_kv_max) {
+  const long long units = (long long)(B > 0 ? B : 1) * (Hkv > 0 ? Hkv : 1);
+  const int tiles = S_kv_max > 0 ? (S_kv_max + 127) / 128 : 1;
+  const long long target = 8LL * 256;  // several work units for each of the 256 compute units
+  long long s = (target + units - 1) / units;
+  if (s > tiles) s = tiles;
+  if (s > 256) s = 256;
+  return s < 1 ? 1 : (int)s;
+}
+
+size_t qfa_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || num_splits <= 0) return 0;
+  return ws_bytes(B, Hq, D, num_splits);
+}
+
+qfa_status qfa_fwd_decode(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                          const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                          int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens, int D,
+                          float softmax_scale, int block_size, int* num_splits, void* workspace,
+                          size_t workspace_bytes, float* O, float* lse, hipStream_t stream) {
+  if (!num_splits || S_kv_max < 0 || *num_splits < 0 || *num_splits > 4096) return QFA_ERR_INVALID_ARG;
+  qfa_status st = check_attn_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, D, softmax_scale,
+                                    block_size, O);
+  if (st != QFA_OK) return st;
+  int splits = *num_splits == 0 ? qfa_decode_default_splits(B, Hkv, S_kv_max) : *num_splits;
+  if (B == 0) {
+    *num_splits = splits;
+    return QFA_OK;
+  }
+  const size_t need = ws_bytes(B, Hq, D, splits);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return QFA_ERR_WORKSPACE;
+  const int G = Hq / Hkv;
+  const long long nwg = (long long)B * Hkv * ((G + 31) / 32) * splits;
+  if (nwg > 0x7FFFFFFFLL) return QFA_ERR_INVALID_ARG;
+  *num_splits = splits;
+  const size_t rows = (size_t)B * Hq * splits;
+  float* Op = static_cast<float*>(workspace);
+  float* Lp = reinterpret_cast<float*>(static_cast<char*>(workspace) + (rows * D * sizeof(float) + 255) / 256 * 256);
+  qfa::AttnArgs a{};
+  a.q4 = q4; a.q4s = q4s; a.k4 = k4; a.k4s = k4s; a.v8 = v8; a.v8s = v8s;
+  a.kbar = kbar; a.qbf = q_bf16; a.kv_lens = kv_lens;
+  a.O = Op; a.lse = Lp;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = 1; a.Skv = S_kv_max; a.D = D; a.G = G;
+  a.causal = 0;
+  a.c2 = softmax_scale * kLog2e;
+  a.num_splits = splits;
+  return from_hip(qfa::launch_decode(a, O, lse, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Internal declarations shared by the HIP translation units of libqfa.
+// gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qfa {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kTile = 128;   // keys per online-softmax step (the running max is updated per tile)
+constexpr int kBlock = 32;   // MX block size
+constexpr int kRows = 32;    // query rows per wave (one 32x32 MFMA column block)
+
+// E8M0 code 127 = 1.0
+constexpr int kScaleOne = 127;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// 2^k for k in [-126, 127] as an exact float.
+__device__ __forceinline__ float exp2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
+// ceil(log2 a) for a finite, positive binary32 value given by its bits.
+__device__ __forceinline__ int ceil_log2_f32bits(uint32_t u) {
+  uint32_t E = u >> 23, M = u & 0x7FFFFFu;
+  if (E == 0) {  // subnormal: a = M * 2^-149
+    int c = (M <= 1u) ? 0 : 32 - __clz(M - 1u);
+    return c - 149;
+  }
+  return (int)E - 127 + (M != 0u);
+}
+
+// Shared E8M0 exponent of an MX block from its (finite) amax bits:
+// ceil(log2 amax) - k clamped to [-127, 127]; amax == 0 -> -127.
+__device__ __forceinline__ int mx_block_exponent(uint32_t amax_bits, int k) {
+  if (amax_bits == 0u) return -127;
+  int e = ceil_log2_f32bits(amax_bits) - k;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// MFMA wrappers (gfx950 block-scaled f8f6f4).  Format codes: 0 = FP8 E4M3, 4 = FP4 E2M1.
+// 32x32x64: lane l supplies row (l % 32) and K-block (l / 32); the scale byte
+// (bits 7:0 of the scale operand) applies to that lane's 32-element K-block.
+__device__ __forceinline__ v16f mfma_fp4_32x32x64(v4i a, v4i b, v16f c, int sa, int sb) {
+  v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+}
+__device__ __forceinline__ v16f mfma_fp8_32x32x64(v8i a, v8i b, v16f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// ---------------------------------------------------------------- launchers (host side)
+hipError_t launch_quant_qk4(const uint16_t* x, int B, int H, int S, int D, int smooth, uint8_t* codes,
+                            uint8_t* scales, uint16_t* kbar, hipStream_t s);
+hipError_t launch_quant_v8(const uint16_t* v, int B, int H, int S, int D, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s);
+
+struct AttnArgs {
+  const uint8_t* q4;
+  const uint8_t* q4s;
+  const uint8_t* k4;
+  const uint8_t* k4s;
+  const uint8_t* v8;
+  const uint8_t* v8s;
+  const uint16_t* kbar;   // may be null
+  const uint16_t* qbf;    // may be null (null iff kbar null)
+  const int32_t* kv_lens; // decode only, may be null
+  float* O;               // prefill: final O; decode: partial O workspace
+  float* lse;             // prefill: final LSE (may be null); decode: partial LSE workspace
+  int B, Hq, Hkv, Sq, Skv, D, G;
+  int causal;
+  float c2;               // softmax_scale * log2(e), rounded to binary32
+  int num_splits;         // decode
+};
+
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode(const AttnArgs& a, float* O, float* lse, hipStream_t s);
+
+}  // namespace qfa

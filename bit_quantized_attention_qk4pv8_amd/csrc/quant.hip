@@ -1,0 +1,184 @@
+// Online block quantisers (HBM-bound, one read of bf16 and one write of codes).
+//
+//  * Q/K -> MXFP4: E2M1 elements, one E8M0 scale per 32 consecutive channels,
+//    exponent ceil(log2 amax) - 2 ("MpFA: Hardware-Efficient Train-Free QK4V8
+//    FlashAttention Kernels on Blackwell GPUs", abstract: online quantisation of
+//    Q and K to 4 bits with block scales; block recipe per the hnwysp.cn
+//    MXAttention/MXFP4 notes, sections 2.3 and 5.2: amax -> power-of-two scale ->
+//    divide -> round to nearest even).
+//  * K smoothing for the rank-one compensation: per 128-token block channel
+//    means, summed exactly in binary64, divided by the number of present tokens
+//    and rounded to bf16; the quantised tensor is fl32(K - Kbar).
+//  * V -> E4M3 with one E8M0 scale per 32 consecutive tokens of one channel
+//    (exponent ceil(log2 amax) - 8), stored block-contiguous [.., S/32, D, 32].
+//
+// The element conversions use gfx950's RNE converters on the exactly
+// pre-scaled value x * 2^-e (a power-of-two multiply, exact).
+#include "qfa_internal.h"
+
+namespace qfa {
+
+// binary64 -> bf16 bits, round to nearest even (correct for every finite value).
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
+  uint64_t u = (uint64_t)__double_as_longlong(d);
+  uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  double a = fabs(d);
+  if (a != a) return 0x7FC0u;
+  if (a == 0.0) return sign;
+  if (a < 1.1754943508222875e-38) {  // below 2^-126: bf16 subnormal, units of 2^-133
+    double n = rint(a * 0x1p133);
+    return sign | (uint16_t)n;
+  }
+  uint64_t ua = u & 0x7FFFFFFFFFFFFFFFull;
+  uint64_t r = ua + 0xFFFFFFFFFFFull + ((ua >> 45) & 1ull);  // drop 45 bits (52 - 7): bias 2^44 - 1 + lsb
+  int ex = (int)(r >> 52) - 1023 + 127;
+  uint32_t man = (uint32_t)(r >> 45) & 0x7Fu;
+  if (ex >= 255) return sign | 0x7F80u;
+  return sign | (uint16_t)((ex << 7) | man);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) k_quant_qk4(const uint16_t* __restrict__ x, int S, int ntiles, int smooth,
+                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                   uint16_t* __restrict__ kbar) {
+  constexpr int NB = D / kBlock;
+  __shared__ float kb[D];
+  const int tile = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int t0 = tile * kTile;
+  const int n = min(kTile, S - t0);
+  const uint16_t* xs = x + (bh * (size_t)S + t0) * D;
+  if (smooth) {
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+      double sum = 0.0;
+      for (int j = 0; j < n; ++j) sum += (double)bf16_bits_to_float(xs[(size_t)j * D + c]);
+      uint16_t b = f64_to_bf16_rne(sum / (double)n);
+      kb[c] = bf16_bits_to_float(b);
+      kbar[(bh * ntiles + tile) * D + c] = b;
+    }
+    __syncthreads();
+  }
+  for (int w = threadIdx.x; w < n * NB; w += blockDim.x) {
+    const int j = w / NB, blk = w % NB;
+    const uint4* src = reinterpret_cast<const uint4*>(xs + (size_t)j * D + blk * kBlock);
+    float v[kBlock];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint4 u = src[q];
+      uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[q * 8 + 2 * k] = bf16_bits_to_float(wds[k] & 0xFFFFu);
+        v[q * 8 + 2 * k + 1] = bf16_bits_to_float(wds[k] >> 16);
+      }
+    }
+    if (smooth) {
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) v[i] = v[i] - kb[blk * kBlock + i];
+    }
+    uint32_t amax = 0u, nonfinite = 0u;
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) {
+      uint32_t a = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+      nonfinite |= (a >= 0x7F800000u);
+      amax = a > amax ? a : amax;
+    }
+    const size_t row = bh * (size_t)S + t0 + j;
+    uint4 out = {0u, 0u, 0u, 0u};
+    uint8_t sc = 0xFF;
+    if (!nonfinite) {
+      const int e = mx_block_exponent(amax, 2);
+      const float inv = exp2i(-e);  // e in [-127, 126] for finite binary32 input
+      uint32_t wd[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t r = 0u;
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 0] * inv, v[q * 8 + 1] * inv, 1.0f, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 2] * inv, v[q * 8 + 3] * inv, 1.0f, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 4] * inv, v[q * 8 + 5] * inv, 1.0f, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 6] * inv, v[q * 8 + 7] * inv, 1.0f, 3);
+        wd[q] = r;
+      }
+      out = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      sc = (uint8_t)(e + 127);
+    }
+    *reinterpret_cast<uint4*>(codes + row * (D / 2) + blk * (kBlock / 2)) = out;
+    scales[row * NB + blk] = sc;
+  }
+}
+
+// One workgroup per (b, h, 32-token block); thread c handles channel c.
+template <int D>
+__global__ void __launch_bounds__(D) k_quant_v8(const uint16_t* __restrict__ v, int S, int nblk,
+                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ uint16_t tile[kBlock * D];
+  const int blk = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int j0 = blk * kBlock;
+  const int n = min(kBlock, S - j0);
+  const uint16_t* src = v + (bh * (size_t)S + j0) * D;
+  // stage the block (n * D bf16, a multiple of 16 bytes) through LDS with 16-byte loads
+  const int chunks = n * D / 8;
+  for (int i = threadIdx.x; i < chunks; i += D)
+    reinterpret_cast<uint4*>(tile)[i] = reinterpret_cast<const uint4*>(src)[i];
+  __syncthreads();
+  const int c = threadIdx.x;
+  float x[kBlock];
+  uint32_t amax = 0u, nonfinite = 0u;
+#pragma unroll
+  for (int t = 0; t < kBlock; ++t) {
+    x[t] = (t < n) ? bf16_bits_to_float(tile[t * D + c]) : 0.0f;
+    uint32_t a = __float_as_uint(x[t]) & 0x7FFFFFFFu;
+    nonfinite |= (a >= 0x7F800000u);
+    amax = a > amax ? a : amax;
+  }
+  uint32_t wd[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  uint8_t sc = 0xFF;
+  if (!nonfinite) {
+    const int e = mx_block_exponent(amax, 8);
+    const float inv = exp2i(-e);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      int r = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q] * inv, x[4 * q + 1] * inv, 0, false);
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2] * inv, x[4 * q + 3] * inv, r, true);
+      wd[q] = (uint32_t)r;
+    }
+    sc = (uint8_t)(e + 127);
+  }
+  uint8_t* dst = codes + ((bh * nblk + blk) * D + c) * kBlock;
+  reinterpret_cast<uint4*>(dst)[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  reinterpret_cast<uint4*>(dst)[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+  scales[(bh * nblk + blk) * D + c] = sc;
+}
+
+hipError_t launch_quant_qk4(const uint16_t* x, int B, int H, int S, int D, int smooth, uint8_t* codes,
+                            uint8_t* scales, uint16_t* kbar, hipStream_t s) {
+  const int ntiles = (S + kTile - 1) / kTile;
+  dim3 grid(ntiles, B * H);
+  switch (D) {
+#define QFA_QK4_CASE(DD) \
+  case DD: hipLaunchKernelGGL(k_quant_qk4<DD>, grid, dim3(256), 0, s, x, S, ntiles, smooth, codes, scales, kbar); break;
+    QFA_QK4_CASE(32) QFA_QK4_CASE(64) QFA_QK4_CASE(96) QFA_QK4_CASE(128) QFA_QK4_CASE(160) QFA_QK4_CASE(192)
+    QFA_QK4_CASE(224) QFA_QK4_CASE(256)
+#undef QFA_QK4_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_v8(const uint16_t* v, int B, int H, int S, int D, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s) {
+  const int nblk = (S + kBlock - 1) / kBlock;
+  dim3 grid(nblk, B * H);
+  switch (D) {
+#define QFA_V8_CASE(DD) \
+  case DD: hipLaunchKernelGGL(k_quant_v8<DD>, grid, dim3(DD), 0, s, v, S, nblk, codes, scales); break;
+    QFA_V8_CASE(32) QFA_V8_CASE(64) QFA_V8_CASE(96) QFA_V8_CASE(128) QFA_V8_CASE(160) QFA_V8_CASE(192)
+    QFA_V8_CASE(224) QFA_V8_CASE(256)
+#undef QFA_V8_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qfa

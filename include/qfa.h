@@ -1,0 +1,153 @@
+/*
+ * qfa.h -- C ABI of the QK4PV8 mixed-precision attention forward library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method ("MpFA: Hardware-Efficient Train-Free QK4V8 FlashAttention Kernels
+ * on Blackwell GPUs", abstract): Q and K are quantised on the fly to 4-bit
+ * floating point with per-block shared scales, S = Q K^T / sqrt(d) runs on the
+ * 4-bit operands, softmax is computed online (running max, running sum, output
+ * rescale) without writing S or P to memory, P and V are quantised to FP8 E4M3
+ * and O = P V accumulates in FP32; an optional rank-one smoothing compensation
+ * adds one extra matrix-multiply term; prefill and split-KV decode are covered
+ * with an adaptive parallel partition.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor arguments are DEVICE pointers to contiguous, 16-byte aligned
+ *    buffers owned by the caller.  The library never allocates, frees or
+ *    retains device memory; buffers must stay alive until `stream` has
+ *    finished the enqueued work.
+ *  - Every call validates its arguments on the host, synchronously.  On any
+ *    error nothing is launched and no output is written.  On success the work
+ *    is enqueued on `stream` (NULL = the legacy default stream) and the call
+ *    returns without synchronising.  Launch failures are reported as
+ *    QFA_ERR_HIP.
+ *  - Stateless and thread-safe; no C++ exception crosses the ABI.
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - MX block size: 32 (`block_size` must be 32).  Head dimension D: 64 or
+ *    128 for attention; any multiple of 32 up to 256 for the quantisers.
+ *  - E8M0 scale codes: value 2^(code - 127); 0xFF marks a block that held a
+ *    NaN or an infinity (its element codes are 0).  Inputs are expected finite.
+ *
+ * Formats (the MXFP4 block of 32 elements with one E8M0 power-of-two scale and
+ * the E2M1 element values 0, 1/2, 1, 3/2, 2, 3, 4, 6 follow the FP4 tutorial
+ * "FlashAttention压到4位", section "FP4 只有约 15 个可表示的数"; the block
+ * quantiser -- amax, power-of-two scale, divide, round to nearest even, store
+ * codes and scales in separate pools -- follows the hnwysp.cn MXAttention /
+ * MXFP4 notes, sections 2.3, 5.2 and 5.4):
+ *  - Q/K codes  [B][H][S][D/2]   E2M1, element 2k in bits 3:0, 2k+1 in bits 7:4
+ *  - Q/K scales [B][H][S][D/32]  E8M0, one per 32 consecutive channels,
+ *                                exponent ceil(log2 amax) - 2 (clamped to
+ *                                [-127, 127]; amax = 0 gives code 0)
+ *  - Kbar       [B][Hkv][ceil(S/128)][D] bf16: channel mean of K over each
+ *                                128-token block (present tokens only)
+ *  - V codes    [B][Hkv][ceil(S/32)][D][32] E4M3 (OCP, bias 7, max 448):
+ *                                the 32 tokens of one MX block of one channel
+ *                                are contiguous; absent tokens of a ragged
+ *                                last block hold code 0
+ *  - V scales   [B][Hkv][ceil(S/32)][D] E8M0, exponent ceil(log2 amax) - 8
+ *  - O          [B][Hq][S_q][D] float32,  LSE [B][Hq][S_q] float32 (natural log)
+ */
+#ifndef QFA_H
+#define QFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qfa_status {
+  QFA_OK = 0,
+  QFA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, Hq % Hkv != 0 */
+  QFA_ERR_UNSUPPORTED = 2, /* D or block_size outside what the kernels support */
+  QFA_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+  QFA_ERR_HIP = 4          /* kernel launch failed (hipGetLastError) */
+} qfa_status;
+
+/*
+ * Online Q or K quantisation to MXFP4 (MpFA abstract: "online quantization";
+ * block quantiser of the MXFP4 notes, sections 2.3 and 5.2).
+ *   x       bf16 [B][H][S][D]
+ *   smooth  0: quantise x.  1 (K only): also write kbar and quantise the
+ *           smoothed tensor fl32(x - Kbar_block) -- the K side of the rank-one
+ *           smoothing compensation.  kbar must be NULL iff smooth == 0.
+ *   codes   out [B][H][S][D/2], scales out [B][H][S][D/32], kbar out as above.
+ * Deterministic: codes, scales and kbar are bit-exact functions of x.
+ */
+qfa_status qfa_quantize_qk4(const uint16_t* x, int B, int H, int S, int D, int block_size, int smooth,
+                            uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t stream);
+
+/*
+ * V quantisation to FP8 E4M3 with one E8M0 scale per (32 consecutive tokens,
+ * channel) -- the contraction axis of P V (MpFA abstract: FP8 for PV).
+ *   v      bf16 [B][H][S][D]
+ *   codes  out [B][H][ceil(S/32)][D][32], scales out [B][H][ceil(S/32)][D].
+ */
+qfa_status qfa_quantize_v8(const uint16_t* v, int B, int H, int S, int D, int block_size, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream);
+
+/*
+ * Prefill forward (MpFA abstract; online softmax per the FP4 tutorial's
+ * section "注意力慢在哪儿").  For each query row i of head h (kv head
+ * h / (Hq/Hkv)) the 128-token key tiles are visited in ascending order:
+ *   s_j = scale * (q4 . k4_j + delta_{i,tile})   (delta = q_bf16 . Kbar_tile,
+ *                                                  only when kbar != NULL)
+ *   m'  = max(m, max_j s_j);  P8_j = E4M3(256 * 2^(log2e * s_j - m'))
+ *   l   = 2^(m - m') l + sum_j P8_j;  O = 2^(m - m') O + sum_j P8_j V8_j
+ * and O / l, LSE = ln(l / 256) + m ln 2 are written.  S and P never reach
+ * memory.  Causal masks are bottom-right aligned: key j is visible to query i
+ * iff j <= i + (S_kv - S_q); a row with no visible key gets O = 0, LSE = -inf.
+ *   q4, q4s      MXFP4 Q [B][Hq][S_q][D/2], [B][Hq][S_q][D/32]
+ *   k4, k4s      MXFP4 K [B][Hkv][S_kv][D/2], [..][D/32] (smoothed if kbar)
+ *   kbar, q_bf16 both NULL (no compensation) or both set:
+ *                kbar [B][Hkv][ceil(S_kv/128)][D] bf16, q_bf16 [B][Hq][S_q][D]
+ *   v8, v8s      E4M3 V and its scales (layout above)
+ *   O            out float32 [B][Hq][S_q][D];  lse out float32 [B][Hq][S_q] or NULL
+ */
+qfa_status qfa_fwd_prefill(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                           const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                           int B, int Hq, int Hkv, int S_q, int S_kv, int D, int causal, float softmax_scale,
+                           int block_size, float* O, float* lse, hipStream_t stream);
+
+/*
+ * Split-KV decode forward, one query token per sequence (MpFA abstract:
+ * adaptive parallel partitioning across prefill and decode).  Sequence b uses
+ * its first L_b = kv_lens[b] keys (kv_lens: device int32 [B], or NULL for
+ * S_kv_max everywhere; 0 <= L_b <= S_kv_max).  Its ceil(L_b/128) tiles are cut
+ * into num_splits contiguous runs of ceil(tiles/num_splits) tiles; each run
+ * yields a normalised partial (O_s, LSE_s) in `workspace`, and a second kernel
+ * merges them: LSE = log sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s.  Runs
+ * with no key get weight 0.  No causal mask.
+ *   q4, q4s        MXFP4 Q [B][Hq][1][D/2], [B][Hq][1][D/32]
+ *   k4, k4s, v8, v8s   the pre-quantised KV cache, S_kv_max tokens per sequence
+ *   kbar, q_bf16   both NULL or both set, as for prefill
+ *   num_splits     in/out: 0 lets the library choose (written back); > 0 is used
+ *   workspace      device buffer of at least qfa_decode_workspace_bytes(...)
+ *   O, lse         out float32 [B][Hq][D], [B][Hq] (lse may be NULL)
+ */
+qfa_status qfa_fwd_decode(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                          const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                          int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens, int D,
+                          float softmax_scale, int block_size, int* num_splits, void* workspace,
+                          size_t workspace_bytes, float* O, float* lse, hipStream_t stream);
+
+/* Bytes of decode workspace for the given shape and split count (> 0). */
+size_t qfa_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
+
+/* The split count the library picks for num_splits == 0 (host arithmetic only):
+ * enough (sequence, kv head, split) work units to give every compute unit
+ * several, never more splits than tiles. */
+int qfa_decode_default_splits(int B, int Hkv, int S_kv_max);
+
+/* Human-readable name of a status code (static storage). */
+const char* qfa_status_string(qfa_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int qfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QFA_H */

@@ -1,0 +1,108 @@
+"""The C-ABI library: exports and host-side validation (no GPU needed).
+
+Only calls that return before any HIP call are made here: version, status
+strings, workspace sizing, the split heuristic, and argument validation that
+rejects the call on the host.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import bit_quantized_attention_qk4pv8_amd as qfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qfa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qfa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_python_exports():
+    assert declared_functions() == sorted(qfa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = qfa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings():
+    assert qfa.qfa_version() == 10000
+    assert qfa.status_string(0) == "QFA_OK"
+    assert qfa.status_string(2) == "QFA_ERR_UNSUPPORTED"
+    assert qfa.status_string(3) == "QFA_ERR_WORKSPACE"
+    assert qfa.status_string(99) == "QFA_ERR_UNKNOWN"
+
+
+def test_workspace_bytes_and_default_splits():
+    # O partials (B*Hq*splits*D floats) and LSE partials, each padded to 256 bytes
+    assert qfa.qfa_decode_workspace_bytes(64, 32, 128, 16) == 64 * 32 * 16 * 128 * 4 + 64 * 32 * 16 * 4
+    assert qfa.qfa_decode_workspace_bytes(1, 1, 64, 1) == 256 + 256
+    assert qfa.qfa_decode_workspace_bytes(0, 32, 128, 16) == 0
+    assert qfa.qfa_decode_default_splits(64, 8, 32768) == 4        # 512 units -> 2048 target
+    assert qfa.qfa_decode_default_splits(1, 8, 32768) == 256       # capped
+    assert qfa.qfa_decode_default_splits(1, 1, 300) == 3           # never more splits than tiles
+    assert qfa.qfa_decode_default_splits(1, 1, 0) == 1
+
+
+def _call_raw(fn, *args):
+    return getattr(qfa.lib(), fn)(*args)
+
+
+def test_validation_rejects_before_launch():
+    P = ctypes.c_void_p
+    fake = P(4096)          # 16-byte aligned, never dereferenced: validation fails first
+    odd = P(4097)
+    # block size and head dimension
+    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 64, 16, 0, fake, fake, None, None) == qfa.QFA_ERR_UNSUPPORTED
+    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 48, 32, 0, fake, fake, None, None) == qfa.QFA_ERR_UNSUPPORTED
+    # kbar must be given iff smooth
+    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 64, 32, 1, fake, fake, None, None) == qfa.QFA_ERR_INVALID_ARG
+    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 64, 32, 0, fake, fake, fake, None) == qfa.QFA_ERR_INVALID_ARG
+    # misaligned input
+    assert _call_raw("qfa_quantize_v8", odd, 1, 1, 1, 64, 32, fake, fake, None) == qfa.QFA_ERR_INVALID_ARG
+    # empty problem: nothing to do
+    assert _call_raw("qfa_quantize_v8", None, 0, 1, 1, 64, 32, None, None, None) == qfa.QFA_OK
+    F = ctypes.c_float
+    pre = lambda Hq, Hkv, D, bs, kbar, qbf, O, scale=0.125: _call_raw(
+        "qfa_fwd_prefill", fake, fake, fake, fake, kbar, qbf, fake, fake, 1, Hq, Hkv, 8, 8, D, 1, F(scale), bs, O,
+        None, None)
+    assert pre(4, 3, 128, 32, None, None, fake) == qfa.QFA_ERR_INVALID_ARG   # Hq % Hkv
+    assert pre(4, 2, 96, 32, None, None, fake) == qfa.QFA_ERR_UNSUPPORTED    # D
+    assert pre(4, 2, 128, 64, None, None, fake) == qfa.QFA_ERR_UNSUPPORTED   # block size
+    assert pre(4, 2, 128, 32, fake, None, fake) == qfa.QFA_ERR_INVALID_ARG   # kbar without q_bf16
+    assert pre(4, 2, 128, 32, None, None, None) == qfa.QFA_ERR_INVALID_ARG   # no output
+    assert pre(4, 2, 128, 32, None, None, fake, scale=0.0) == qfa.QFA_ERR_INVALID_ARG
+    # decode: workspace too small is reported before launch
+    ns = ctypes.c_int(4)
+    st = _call_raw("qfa_fwd_decode", fake, fake, fake, fake, None, None, fake, fake, 2, 8, 2, 1024, None, 128,
+                   F(0.1), 32, ctypes.byref(ns), fake, ctypes.c_size_t(16), fake, None, None)
+    assert st == qfa.QFA_ERR_WORKSPACE
+    st = _call_raw("qfa_fwd_decode", fake, fake, fake, fake, None, None, fake, fake, 2, 8, 2, 1024, None, 128,
+                   F(0.1), 32, None, fake, ctypes.c_size_t(1 << 30), fake, None, None)
+    assert st == qfa.QFA_ERR_INVALID_ARG
+
+
+def test_kv_cache_byte_formula_matches_printed_example():
+    """Byte accounting used for the decode roofline reproduces the KV-cache
+    formula example printed in the MXFP4 notes (section 1.1)."""
+    from bit_quantized_attention_qk4pv8_amd.roofline import kv_cache_bytes, decode_algorithmic_bytes
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "kv_cache_bytes.json")))
+    per_tok_layer = kv_cache_bytes(layers=1, kv_heads=g["kv_heads"], head_dim=g["head_dim"], seq_len=1,
+                                   bytes_per_element=g["bytes_per_element"], batch=1)
+    assert per_tok_layer == g["bytes_per_token_per_layer"]
+    assert kv_cache_bytes(g["layers"], g["kv_heads"], g["head_dim"], 1, g["bytes_per_element"], 1) == \
+        g["bytes_per_token_all_layers"]
+    assert kv_cache_bytes(g["layers"], g["kv_heads"], g["head_dim"], g["seq_len"], g["bytes_per_element"],
+                          g["batch"]) == g["total_bytes_128k"]
+    # QK4 / V8 with E8M0 scales: 64 + 4 + 128 + 4 = 200 bytes per token per kv head at D = 128
+    assert decode_algorithmic_bytes(B=1, Hq=1, Hkv=1, L=1, D=128, include_q_o=False) == 200
+    assert decode_algorithmic_bytes(B=64, Hq=32, Hkv=8, L=32768, D=128) == 3357016064

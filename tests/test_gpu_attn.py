@@ -1,0 +1,193 @@
+"""GPU prefill and split-KV decode vs the oracle (c).
+
+Small shapes compare every row (several tiles, ragged tails, GQA packing,
+head chunks, bottom-right causal alignment, rows with no visible key, the
+compensation term across a 32-tile boundary).  Full workload sizes run the
+kernels exactly as the benchmark launches them and compare sampled rows.
+Bar: O within 3e-3 max-abs and 1e-3 relative L2 of the oracle; LSE within
+1e-3; error against exact FP64 attention is reported, not gated.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_attention_qk4pv8_amd as qfa
+import oracle
+from bit_quantized_attention_qk4pv8_amd.workloads import WORKLOADS, Workload, bf16_bits, make_inputs
+from gpu_util import compare_o, sample_rows, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed, k_offset=0.0, q_scale=1.0):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randn((B, Hq, Sq, D), generator=g, device="cuda") * q_scale
+    k = torch.randn((B, Hkv, Skv, D), generator=g, device="cuda")
+    if k_offset:
+        k += torch.randn((B, Hkv, 1, D), generator=g, device="cuda") * k_offset
+    v = torch.randn((B, Hkv, Skv, D), generator=g, device="cuda")
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def _gpu_prefill(q, k, v, causal, scale, smooth):
+    B, Hq, Sq, D = q.shape
+    Skv = k.shape[2]
+    q4, q4s, _ = qfa.quantize_qk4(q)
+    k4, k4s, kbar = qfa.quantize_qk4(k, smooth=smooth)
+    v8, v8s = qfa.quantize_v8(v)
+    O, lse = qfa.fwd_prefill(q4, q4s, k4, k4s, v8, v8s, Skv, causal, scale, kbar=kbar,
+                             q_bf16=q if smooth else None)
+    torch.cuda.synchronize()
+    return O, lse
+
+
+def _check_prefill(q, k, v, causal, scale, smooth, rows, label):
+    B, Hq, Sq, D = q.shape
+    say("prefill", label, "q", tuple(q.shape), "k", tuple(k.shape), "causal", causal, "smooth", smooth)
+    O, lse = _gpu_prefill(q, k, v, causal, scale, smooth)
+    res = oracle.prefill_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, causal, scale, smooth=smooth)
+    Og = to_np(O)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    lg = to_np(lse)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    compare_o(Og, res["O_q"], lg, res["lse_q"], label)
+    ok = np.isfinite(res["lse_x"])
+    if ok.any():
+        ex = res["O_x"][ok]
+        err = np.linalg.norm(Og[ok] - ex) / np.linalg.norm(ex)
+        cos = float(np.sum(Og[ok] * ex) / (np.linalg.norm(Og[ok]) * np.linalg.norm(ex)))
+        say("%s vs exact FP64: rel-L2 %.3e cosine %.6f (reported only)" % (label, err, cos))
+    return O, lse
+
+
+def _all_rows(B, H, S):
+    return np.array([(b, h, i) for b in range(B) for h in range(H) for i in range(S)], dtype=np.int64)
+
+
+CASES = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, smooth, k_offset, label
+    (1, 2, 2, 256, 256, 64, False, False, 0.0, "tiny-shape"),
+    (1, 4, 2, 300, 300, 128, True, False, 0.0, "causal-ragged-D128"),
+    (1, 5, 1, 70, 333, 64, True, False, 0.0, "bottom-right-G5-D64"),
+    (1, 2, 2, 100, 64, 128, True, False, 0.0, "sq>skv-empty-rows"),
+    (1, 4, 1, 700, 700, 128, True, True, 3.0, "compensation-causal"),
+    (1, 16, 2, 45, 1000, 128, False, False, 0.0, "noncausal-G8"),
+    (1, 12, 1, 200, 200, 128, True, False, 0.0, "G12-two-head-chunks"),
+    (2, 4, 4, 130, 130, 64, True, True, 3.0, "batch2-comp-D64"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[-1] for c in CASES])
+def test_prefill_small_all_rows(case):
+    B, Hq, Hkv, Sq, Skv, D, causal, smooth, koff, label = case
+    q, k, v = _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed=zlib.crc32(label.encode()) % 1000, k_offset=koff, q_scale=2.0)
+    _check_prefill(q, k, v, causal, 1.0 / math.sqrt(D), smooth, _all_rows(B, Hq, Sq), label)
+
+
+def test_prefill_tiny_workload():
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w, seed=0)
+    _check_prefill(inp["q"], inp["k"], inp["v"], w.causal, w.scale, w.smooth, _all_rows(1, w.Hq, w.S_q), "tiny")
+
+
+def test_prefill_compensation_beyond_32_tiles():
+    """Delta is recomputed every 32 key tiles (4096 keys): 64 rows over 5000 keys."""
+    q, k, v = _rand_inputs(1, 2, 1, 64, 5000, 128, seed=77, k_offset=3.0)
+    _check_prefill(q, k, v, False, 1 / math.sqrt(128), True, _all_rows(1, 2, 64), "comp-5000keys")
+
+
+def test_prefill_deterministic():
+    q, k, v = _rand_inputs(1, 4, 2, 300, 300, 128, seed=5)
+    O1, l1 = _gpu_prefill(q, k, v, True, 0.088, False)
+    O2, l2 = _gpu_prefill(q, k, v, True, 0.088, False)
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name,nrows", [("llama16k", 384), ("qwen32k", 320), ("long128k", 192)])
+def test_prefill_workload_sampled(name, nrows):
+    w = WORKLOADS[name]
+    inp = make_inputs(w, seed=0)
+    rows = sample_rows(1, w.Hq, w.S_q, nrows, seed=1, must=(0, 127, 128, 4095))
+    _check_prefill(inp["q"], inp["k"], inp["v"], w.causal, w.scale, w.smooth, rows, name)
+
+
+# ----------------------------------------------------------------------------- decode
+def _gpu_decode(q, k, v, num_splits, kv_lens=None, smooth=False):
+    B, Hq, _, D = q.shape
+    Smax = k.shape[2]
+    q4, q4s, _ = qfa.quantize_qk4(q)
+    k4, k4s, kbar = qfa.quantize_qk4(k, smooth=smooth)
+    v8, v8s = qfa.quantize_v8(v)
+    lens = None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32, device="cuda")
+    O, lse, used = qfa.fwd_decode(q4, q4s, k4, k4s, v8, v8s, Smax, 1 / math.sqrt(D), num_splits=num_splits,
+                                  kv_lens=lens, kbar=kbar, q_bf16=q if smooth else None)
+    torch.cuda.synchronize()
+    return O, lse, used
+
+
+def _check_decode(q, k, v, num_splits, kv_lens=None, label="", seqs=None, smooth=False):
+    B, Hq, _, D = q.shape
+    say("decode", label, "q", tuple(q.shape), "k", tuple(k.shape), "splits", num_splits)
+    O, lse, used = _gpu_decode(q, k, v, num_splits, kv_lens, smooth)
+    if num_splits:
+        assert used == num_splits
+    seqs = list(range(B)) if seqs is None else seqs
+    rows = np.array([(b, h, 0) for b in seqs for h in range(Hq)], dtype=np.int64)
+    if smooth:
+        res = _decode_oracle_smooth(q, k, v, rows, used, kv_lens)
+    else:
+        res = oracle.decode_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, 1 / math.sqrt(D), used,
+                                 kv_lens=kv_lens)
+    Og = to_np(O)[rows[:, 0], rows[:, 1]]
+    lg = to_np(lse)[rows[:, 0], rows[:, 1]]
+    compare_o(Og, res["O_q"], lg, res["lse_q"], label)
+    return used
+
+
+def _decode_oracle_smooth(q, k, v, rows, splits, kv_lens):
+    """Oracle decode with K smoothing: quantise with the oracle, run the split schedule."""
+    qb, kb, vb = bf16_bits(q), bf16_bits(k), bf16_bits(v)
+    B, Hq, _, D = qb.shape
+    Hkv, Smax = kb.shape[1], kb.shape[2]
+    G = Hq // Hkv
+    out = {"O_q": np.zeros((len(rows), D)), "lse_q": np.zeros(len(rows))}
+    for n, (b, h, _) in enumerate(rows):
+        g = h // G
+        L = Smax if kv_lens is None else kv_lens[b]
+        nt = (L + 127) // 128
+        per = max(1, -(-nt // splits))
+        kc, ks, kbar = oracle.quantize_qk4(np.ascontiguousarray(kb[b:b + 1, g:g + 1, :L]), smooth=True)
+        vc, vs = oracle.quantize_v8(np.ascontiguousarray(vb[b:b + 1, g:g + 1, :L]))
+        qc, qs, _ = oracle.quantize_qk4(np.ascontiguousarray(qb[b:b + 1, h:h + 1]))
+        O, l = oracle.attn_quant_rows(oracle.dequant_qk4(qc, qs)[0, 0], np.zeros(1, np.int64),
+                                      oracle.dequant_qk4(kc, ks)[0, 0], oracle.dequant_v8(vc[0, 0], vs[0, 0], L),
+                                      1, False, 1 / math.sqrt(D), Qc=oracle.bf16_to_f64(qb[b, h]),
+                                      Kbar=oracle.bf16_to_f64(kbar[0, 0]), split_tiles=per)
+        out["O_q"][n] = O[0]
+        out["lse_q"][n] = l[0]
+    return out
+
+
+@pytest.mark.parametrize("splits", [3, 0, 1])
+def test_decode_small_varlen(splits):
+    q, k, v = _rand_inputs(3, 8, 2, 1, 1000, 128, seed=11, q_scale=2.0)
+    _check_decode(q, k, v, splits, kv_lens=[1000, 517, 0], label="varlen-splits%d" % splits)
+
+
+def test_decode_d64_and_more_splits_than_tiles():
+    q, k, v = _rand_inputs(2, 4, 4, 1, 300, 64, seed=12)
+    _check_decode(q, k, v, 7, label="d64-7splits")   # 3 tiles: splits 3..6 are empty
+
+
+def test_decode_compensation():
+    q, k, v = _rand_inputs(2, 4, 1, 1, 5000, 128, seed=13, k_offset=3.0)
+    _check_decode(q, k, v, 2, label="decode-comp", smooth=True)
+
+
+def test_decode_workload_sampled_sequences():
+    w = WORKLOADS["decode"]
+    inp = make_inputs(w, seed=0)
+    used = _check_decode(inp["q"], inp["k"], inp["v"], w.num_splits, label="decode-B64",
+                         seqs=[0, 17, 42, 63])
+    assert used == 16

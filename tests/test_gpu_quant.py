@@ -1,0 +1,85 @@
+"""GPU quantisers vs the oracle: codes, scales and Kbar must be bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_attention_qk4pv8_amd as qfa
+import oracle
+from bit_quantized_attention_qk4pv8_amd.workloads import WORKLOADS, bf16_bits, make_inputs
+from gpu_util import say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_qk4(x: torch.Tensor, smooth: bool, label: str):
+    say("quantize_qk4", label, tuple(x.shape), "smooth", smooth)
+    codes, scales, kbar = qfa.quantize_qk4(x, smooth=smooth)
+    torch.cuda.synchronize()
+    oc, os_, ok = oracle.quantize_qk4(bf16_bits(x), smooth=smooth)
+    assert np.array_equal(to_np(codes), oc), label + ": codes differ"
+    assert np.array_equal(to_np(scales), os_), label + ": scales differ"
+    if smooth:
+        assert np.array_equal(to_np(kbar.view(torch.int16)).view(np.uint16), ok), label + ": kbar differs"
+
+
+def _check_v8(v: torch.Tensor, label: str):
+    say("quantize_v8", label, tuple(v.shape))
+    codes, scales = qfa.quantize_v8(v)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize_v8(bf16_bits(v))
+    assert np.array_equal(to_np(codes), oc), label + ": codes differ"
+    assert np.array_equal(to_np(scales), os_), label + ": scales differ"
+
+
+@pytest.mark.parametrize("shape,smooth", [((1, 2, 300, 64), False), ((1, 3, 1000, 128), False),
+                                          ((2, 2, 300, 128), True), ((1, 1, 77, 256), True),
+                                          ((1, 1, 5, 32), False)])
+def test_qk4_bitexact_shapes(shape, smooth):
+    g = torch.Generator(device="cuda").manual_seed(sum(shape))
+    x = torch.randn(shape, generator=g, device="cuda")
+    x[..., 3] *= 40.0                                             # outlier channel
+    x[..., 0, :] = 0.0                                            # all-zero row
+    x += torch.randn((1, shape[1], 1, shape[3]), generator=g, device="cuda") * 3.0 * smooth
+    _check_qk4(x.to(torch.bfloat16), smooth, "shape%s" % (shape,))
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 75, 64), (2, 3, 1000, 128), (1, 1, 31, 128), (1, 1, 64, 256)])
+def test_v8_bitexact_shapes(shape):
+    g = torch.Generator(device="cuda").manual_seed(sum(shape) + 1)
+    v = torch.randn(shape, generator=g, device="cuda")
+    v[..., 5, :] *= 100.0
+    v[..., :, 7] *= 1e-3
+    _check_v8(v.to(torch.bfloat16), "shape%s" % (shape,))
+
+
+def test_quantizers_nonfinite_and_tiny():
+    x = torch.randn((1, 1, 64, 128), device="cuda")
+    x[0, 0, 1, 5] = float("nan")
+    x[0, 0, 2, 100] = float("inf")
+    x[0, 0, 3, :32] = 1e-39                 # bf16 subnormals
+    x[0, 0, 4, 32:64] = -0.0
+    xb = x.to(torch.bfloat16)
+    _check_qk4(xb, False, "nonfinite")
+    _check_v8(xb, "nonfinite")
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama16k", "qwen32k"])
+def test_workload_tensors_bitexact(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w, seed=0)
+    _check_qk4(inp["q"], False, name + ".q")
+    _check_qk4(inp["k"], w.smooth, name + ".k")
+    _check_v8(inp["v"], name + ".v")
+
+
+def test_long128k_and_decode_slices_bitexact():
+    w = WORKLOADS["long128k"]
+    inp = make_inputs(w, seed=0)
+    _check_qk4(inp["k"][:, :2].contiguous(), False, "long128k.k[:2]")
+    _check_v8(inp["v"][:, 6:].contiguous(), "long128k.v[6:]")
+    _check_qk4(inp["q"][:, 5:7].contiguous(), False, "long128k.q[5:7]")
+    del inp
+    wd = WORKLOADS["decode"]
+    inp = make_inputs(wd, seed=0, B_override=3)
+    _check_qk4(inp["k"], False, "decode.k")
+    _check_v8(inp["v"], "decode.v")
