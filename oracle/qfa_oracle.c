@@ -39,10 +39,15 @@
  *  - Element rounding: round-to-nearest, ties to the even code, applied once to
  *    the exact value x * 2^-e; the sign of zero is kept; magnitudes beyond the
  *    largest finite value saturate to it.
- *  - P is E4M3(256 * 2^(s - m)) with m the running max (log2 units) updated
- *    after every 128-token key tile in ascending order; the denominator l sums
- *    the decoded P codes.  O is returned in binary64 here, LSE in natural-log
- *    units referring to the compensated logits.
+ *  - P is E4M3(256 * 2^(s - m)) with m the running max in log2 units kept on
+ *    the integer grid: after every 128-token key tile (ascending order)
+ *    m <- max(m, ceil(max_j s_j)).  Online softmax only needs m to bound the
+ *    row max from above; an integer m makes every rescale factor 2^(m - m')
+ *    an exact power of two and, because E4M3 rounding commutes with powers of
+ *    two, makes the P codes independent of the tile and split schedule (up to
+ *    the subnormal range).  The denominator l sums the decoded P codes.  O is
+ *    returned in binary64 here, LSE in natural-log units referring to the
+ *    compensated logits.
  *  - Rank-one smoothing compensation: K is smoothed per 128-token block by its
  *    channel mean Kbar (rounded to bf16); every logit of a block gets back the
  *    rank-one term q_bf16 . Kbar_block.
@@ -399,7 +404,7 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
        * delta32 = fl32(c2 * fl32(delta)), m_tile = fma(max S, c2, delta32),
        * beta = fl32(delta32 - m') */
       float d32 = c2f * (float)delta;
-      float mt = fmaf((float)smax, c2f, d32);
+      float mt = ceilf(fmaf((float)smax, c2f, d32));
       float mn = (m == -INFINITY || mt > (float)m) ? mt : (float)m;
       float beta = d32 - mn;
       alpha = (m == -INFINITY) ? 0.0 : exp2(m - (double)mn);
@@ -414,7 +419,7 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
         P[j] = quantize_p ? orc_e4m3_value(orc_e4m3_encode(p)) : p;
       }
     } else {
-      double mt = c2d * (smax + delta);
+      double mt = ceil(c2d * (smax + delta));
       mnew = (mt > m) ? mt : m;
       alpha = (m == -INFINITY) ? 0.0 : exp2(m - mnew);
       for (int64_t j = 0; j < j1 - j0; ++j) {
