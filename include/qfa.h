@@ -94,9 +94,14 @@ qfa_status qfa_quantize_v8(const uint16_t* v, int B, int H, int S, int D, int bl
  * h / (Hq/Hkv)) the 128-token key tiles are visited in ascending order:
  *   s_j = scale * (q4 . k4_j + delta_{i,tile})   (delta = q_bf16 . Kbar_tile,
  *                                                  only when kbar != NULL)
- *   m'  = max(m, max_j s_j);  P8_j = E4M3(256 * 2^(log2e * s_j - m'))
+ *   m'  = max(m, ceil(max_j log2e * s_j))   (log2 units, an integer bound
+ *                                             on the row max)
+ *   P8_j = E4M3(256 * 2^(log2e * s_j - m'))
  *   l   = 2^(m - m') l + sum_j P8_j;  O = 2^(m - m') O + sum_j P8_j V8_j
- * and O / l, LSE = ln(l / 256) + m ln 2 are written.  S and P never reach
+ * and O / l, LSE = ln(l / 256) + m ln 2 are written.  Because m is an integer
+ * the rescale factors are exact powers of two and the P codes do not depend
+ * on how the key range is cut into tiles or splits.  delta is the exactly
+ * rounded binary32 value of the bf16 dot product.  S and P never reach
  * memory.  Causal masks are bottom-right aligned: key j is visible to query i
  * iff j <= i + (S_kv - S_q); a row with no visible key gets O = 0, LSE = -inf.
  *   q4, q4s      MXFP4 Q [B][Hq][S_q][D/2], [B][Hq][S_q][D/32]
