@@ -2,6 +2,7 @@
 """Benchmark of the QK4PV8 attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--only all|prefill|decode|copy]
 
 One step = the whole prefill hot path over the Llama-3.1-8B-shaped workload
 (B1, Hq32/Hkv8, S16384, D128, causal; bf16 inputs resident in HBM): quantise Q
@@ -14,7 +15,12 @@ is timed in the same run and reported under "decode" as KV GB/s.
 The roofline object is for the dominant kernel (the prefill kernel), timed
 with HIP events on the stream it is launched on; its peak is the blended
 MXFP4 (Q K^T) / FP8 (P V) MFMA peak.  The CPU baseline is the oracle timed on
-a bounded sample of rows of the same workload on this host.
+a bounded sample of rows of the same workload on this host (about 15 s).
+
+`--only prefill|decode` runs just that half (for hardware-counter passes);
+`--only copy` runs a plain device-to-device copy of 1 GiB, the reference
+kernel of known size that scales the FETCH_SIZE / WRITE_SIZE counters into
+bytes.
 """
 import argparse
 import hashlib
@@ -32,11 +38,36 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--workload", default="llama16k")
+    p.add_argument("--only", default="all", choices=("all", "prefill", "decode", "copy"))
     return p.parse_args()
+
+
+COPY_BYTES = 1 << 30
+CPU_TARGET_S = 15.0
+
+
+def run_copy(args):
+    """A plain 1 GiB device copy, timed like the attention kernels; its counter
+    readings calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "ms": round(ms, 4),
+                      "GB/s": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def source_hash():
@@ -68,6 +99,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(each GPU would run its own shard with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.only == "copy":
+        run_copy(args)
+        return
 
     import numpy as np
     import torch
@@ -79,74 +113,77 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = WORKLOADS[args.workload]
-    inp = make_inputs(w, seed=0, device=dev)
-    q, k, v = inp["q"], inp["k"], inp["v"]
-    B, Hq, Hkv, S, D = w.B, w.Hq, w.Hkv, w.S_q, w.D
-    nt = (S + 127) // 128
-    q4 = torch.empty((B, Hq, S, D // 2), dtype=torch.uint8, device=dev)
-    q4s = torch.empty((B, Hq, S, D // 32), dtype=torch.uint8, device=dev)
-    k4 = torch.empty((B, Hkv, S, D // 2), dtype=torch.uint8, device=dev)
-    k4s = torch.empty((B, Hkv, S, D // 32), dtype=torch.uint8, device=dev)
-    kbar = torch.empty((B, Hkv, nt, D), dtype=torch.bfloat16, device=dev) if w.smooth else None
-    v8 = torch.empty((B, Hkv, (S + 31) // 32, D, 32), dtype=torch.uint8, device=dev)
-    v8s = torch.empty((B, Hkv, (S + 31) // 32, D), dtype=torch.uint8, device=dev)
-    O = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-
-    def step(i=None):
-        qfa.qfa_quantize_qk4(q, B, Hq, S, D, 32, 0, q4, q4s, None, stream)
-        qfa.qfa_quantize_qk4(k, B, Hkv, S, D, 32, int(w.smooth), k4, k4s, kbar, stream)
-        qfa.qfa_quantize_v8(v, B, Hkv, S, D, 32, v8, v8s, stream)
-        if i is not None:
-            ev[i][0].record(stream)
-        qfa.qfa_fwd_prefill(q4, q4s, k4, k4s, kbar, q if w.smooth else None, v8, v8s, B, Hq, Hkv, S, S, D,
-                            int(w.causal), w.scale, 32, O, lse, stream)
-        if i is not None:
-            ev[i][1].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    flops = w.flops()
-    comp = w.comp_flops()
-    value = flops / (ms_step * 1e-3) / 1e12
-    achieved = (flops + comp) / (kern_ms * 1e-3) / 1e12
-    peak = rl.blended_peak(flops, comp) / 1e12
+    out = {}
     src = source_hash()
-    traffic = traffic_from_profile("prefill_%s_traffic.json" % w.name, src)
-    out = {
-        "metric": "QK4PV8 fwd prefill TFLOP/s (+ decode KV GB/s) on 1xMI355X",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "mxfp4(QK)+fp8(PV), fp32 accumulate",
-        "data": "synthetic seeded bf16 inputs shaped like Llama-3.1-8B attention (no weights/datasets)",
-        "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "S_q": S, "S_kv": S, "D": D,
-                   "causal": w.causal, "compensation": w.smooth,
-                   "step": "quantize Q,K (MXFP4) + V (FP8) + fused prefill"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 2), "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "qfa::k_prefill<128,%s>" % ("true" if w.smooth else "false"),
-                     "kernel_ms": round(kern_ms, 4), "algorithmic_flop_per_launch": flops + comp},
-    }
-    del O, lse
+    stream = torch.cuda.current_stream()
+    if args.only in ("all", "prefill"):
+        inp = make_inputs(w, seed=0, device=dev)
+        q, k, v = inp["q"], inp["k"], inp["v"]
+        B, Hq, Hkv, S, D = w.B, w.Hq, w.Hkv, w.S_q, w.D
+        nt = (S + 127) // 128
+        q4 = torch.empty((B, Hq, S, D // 2), dtype=torch.uint8, device=dev)
+        q4s = torch.empty((B, Hq, S, D // 32), dtype=torch.uint8, device=dev)
+        k4 = torch.empty((B, Hkv, S, D // 2), dtype=torch.uint8, device=dev)
+        k4s = torch.empty((B, Hkv, S, D // 32), dtype=torch.uint8, device=dev)
+        kbar = torch.empty((B, Hkv, nt, D), dtype=torch.bfloat16, device=dev) if w.smooth else None
+        v8 = torch.empty((B, Hkv, (S + 31) // 32, D, 32), dtype=torch.uint8, device=dev)
+        v8s = torch.empty((B, Hkv, (S + 31) // 32, D), dtype=torch.uint8, device=dev)
+        O = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+        def step(i=None):
+            qfa.qfa_quantize_qk4(q, B, Hq, S, D, 32, 0, q4, q4s, None, stream)
+            qfa.qfa_quantize_qk4(k, B, Hkv, S, D, 32, int(w.smooth), k4, k4s, kbar, stream)
+            qfa.qfa_quantize_v8(v, B, Hkv, S, D, 32, v8, v8s, stream)
+            if i is not None:
+                ev[i][0].record(stream)
+            qfa.qfa_fwd_prefill(q4, q4s, k4, k4s, kbar, q if w.smooth else None, v8, v8s, B, Hq, Hkv, S, S, D,
+                                int(w.causal), w.scale, 32, O, lse, stream)
+            if i is not None:
+                ev[i][1].record(stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_step = (t1 - t0) * 1e3 / args.steps
+        kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        flops = w.flops()
+        comp = w.comp_flops()
+        value = flops / (ms_step * 1e-3) / 1e12
+        achieved = (flops + comp) / (kern_ms * 1e-3) / 1e12
+        peak = rl.blended_peak(flops, comp) / 1e12
+        traffic = traffic_from_profile("prefill_%s_traffic.json" % w.name, src)
+        out.update({
+            "metric": "QK4PV8 fwd prefill TFLOP/s + decode KV GB/s on 1\u00d7MI355X; % roofline",
+            "value": round(value, 2),
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "mxfp4(QK)+fp8(PV), fp32 accumulate",
+            "data": "synthetic seeded bf16 inputs shaped like Llama-3.1-8B attention (no weights/datasets)",
+            "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "S_q": S, "S_kv": S, "D": D,
+                       "causal": w.causal, "compensation": w.smooth,
+                       "step": "quantize Q,K (MXFP4) + V (FP8) + fused prefill"},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 2), "unit": "TFLOP/s",
+                         "frac": round(achieved / peak, 4), "traffic": traffic,
+                         "kernel": "qfa::k_prefill<128,%s>" % ("true" if w.smooth else "false"),
+                         "kernel_ms": round(kern_ms, 4), "algorithmic_flop_per_launch": flops + comp},
+        })
+        del O, lse
     # ------------------------------------------------------------------ decode half
-    if not args.no_decode:
+    if args.only in ("all", "decode") and not args.no_decode:
         wd = WORKLOADS["decode"]
         di = make_inputs(wd, seed=0, device=dev)
         Bd, Hqd, Hkvd, L, Dd = di["B"], wd.Hq, wd.Hkv, wd.S_kv, wd.D
@@ -199,26 +236,39 @@ def main():
         }
         del k4d, v8d, ws
     # ------------------------------------------------------------------ CPU baseline (oracle)
-    if not args.no_cpu_baseline:
+    if args.only in ("all", "prefill") and not args.no_cpu_baseline:
         import oracle
         qb = bf16_bits(q)
         kb = bf16_bits(k)
         vb = bf16_bits(v)
+        del q, k, v, inp
         rng = np.random.default_rng(0)
-        # a bounded sample: whole query heads cost too much; take rows spread over positions
-        n_rows = 48
-        rows = np.stack([np.zeros(n_rows, np.int64), rng.integers(0, Hq, n_rows),
-                         rng.integers(0, S, n_rows)], axis=1)
-        tc0 = time.perf_counter()
-        oracle.prefill_rows(qb, kb, vb, rows, w.causal, w.scale, smooth=w.smooth, exact=False)
-        tc1 = time.perf_counter()
-        sample_pairs = int(sum((r[2] + 1) if w.causal else S for r in rows))
-        cpu_tflops = 4.0 * D * sample_pairs / (tc1 - tc0) / 1e12
+
+        def sample(n_rows):
+            # query rows spread over heads and positions; each call also quantises
+            # the K/V head and the Q heads its rows touch, as the oracle does
+            rows = np.stack([np.zeros(n_rows, np.int64), rng.integers(0, Hq, n_rows),
+                             rng.integers(0, S, n_rows)], axis=1)
+            tc0 = time.perf_counter()
+            oracle.prefill_rows(qb, kb, vb, rows, w.causal, w.scale, smooth=w.smooth, exact=False)
+            dt = time.perf_counter() - tc0
+            pairs = int(sum((r[2] + 1) if w.causal else S for r in rows))
+            return dt, pairs
+
+        # grow the sample until one call takes CPU_TARGET_S / 2 or more (only the
+        # last call is reported; each call quantises the heads it touches again)
+        n_rows = 64
+        while True:
+            dt, pairs = sample(n_rows)
+            if dt >= CPU_TARGET_S / 2 or n_rows >= 16384:
+                break
+            n_rows = int(min(16384, n_rows * min(16.0, CPU_TARGET_S / max(dt, 1e-3))))
+        cpu_tflops = 4.0 * D * pairs / dt / 1e12
         out["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
                                "kind": "oracle",
-                               "sample": "%d random query rows of %s (all their visible keys), including "
-                                         "quantising the K/V heads and Q heads they touch; %.1f s" %
-                                         (n_rows, w.name, tc1 - tc0)}
+                               "sample": "%d random query rows of %s (all %d of their visible query/key pairs), "
+                                         "including the oracle quantising the K/V and Q heads they touch; %.1f s"
+                                         % (n_rows, w.name, pairs, dt)}
     print(json.dumps(out), flush=True)
 
 
