@@ -72,7 +72,7 @@ def run_copy(args):
 
 def source_hash():
     h = hashlib.sha256()
-    for f in ("attn.hip", "quant.hip", "api.hip", "qfa_internal.h"):
+    for f in ("attn.hip", "prefill.hip", "attn_common.h", "quant.hip", "api.hip", "qfa_internal.h"):
         with open(os.path.join(ROOT, "bit_quantized_attention_qk4pv8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -10,6 +10,7 @@ hipcc cross-compiles without a GPU.  Flags:
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import subprocess
 import sys
@@ -18,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqfa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "quant.hip", "attn.hip"]
+SOURCES = ["api.hip", "quant.hip", "attn.hip", "prefill.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -40,6 +41,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
+    # Loading resolves every symbol (no GPU needed): a kernel whose host launch
+    # stub went missing shows up here rather than at the first call.
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError("built library does not load: %s" % e)
     os.replace(tmp, LIB)
     return LIB
 

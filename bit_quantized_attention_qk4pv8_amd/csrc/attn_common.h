@@ -1,0 +1,489 @@
+// Building blocks shared by the prefill and decode attention kernels (gfx950).
+//
+// A 128-key tile is processed by one wave for 32 query rows in three steps:
+//   S^T = K Q^T   on v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1 x E2M1, E8M0 block
+//                 scales fed to the instruction)                 [qk_tile]
+//   softmax       mask, running max on the integer grid, P = E4M3(256 * 2^(.))
+//                 packed directly as the B operand of the P V product
+//                                                                [softmax_tile]
+//   P V           O^T += V^T P^T and the denominator 1 . P^T on the FP8 MFMA,
+//                 with the rescale 2^(m - m_ref) riding on P's E8M0 scale
+//                                                                [pv_tile]
+// pv_then_qk runs the P V of one tile and the S^T of the next back to back.
+// Method: "MpFA: Hardware-Efficient Train-Free QK4V8 FlashAttention Kernels on
+// Blackwell GPUs" (abstract); online softmax per the FP4 tutorial
+// "FlashAttention压到4位", section "注意力慢在哪儿"; the denominator uses the
+// rounded P codes (same tutorial, section "Direct-P").
+#pragma once
+
+#include "qfa_internal.h"
+
+namespace qfa {
+
+// LDS image of one K/V tile (128 keys):
+//   K region [K codes 128 x D/2][K scales, 1 KB area]
+//   V region [V codes 4 x D x 32][V scales, 1 KB area]
+// The two regions may live in separate buffers (KREG / VREG bytes each).
+// K and V codes are stored with an XOR swizzle of their 16-byte chunks (see
+// kswz / vswz) so that the MFMA operand reads are free of bank conflicts.
+template <int D>
+struct TileLayout {
+  static constexpr int KC = kTile * D / 2;
+  static constexpr int KS_BYTES = kTile * D / 32;
+  static constexpr int VC = kTile * D;
+  static constexpr int VS_BYTES = (kTile / 32) * D;
+  static constexpr int K_OFF = 0;
+  static constexpr int KS_OFF = KC;
+  static constexpr int V_OFF = KC + 1024;
+  static constexpr int VS_OFF = V_OFF + VC;
+  static constexpr int STRIDE = VS_OFF + 1024;
+  static constexpr int KREG = KC + 1024;  // K region bytes (codes, then scales at KC)
+  static constexpr int VREG = VC + 1024;  // V region bytes (codes, then scales at VC)
+  static constexpr int NK = KC / 1024;  // 1 KB DMA instructions per region
+  static constexpr int NV = VC / 1024;
+  static constexpr int NKS = D == 128 ? 2 : 1;  // dword DMA instructions (256 B each) for K scales
+  static constexpr int NINS = NK + NKS + NV + 1;
+};
+
+// Token of MFMA row rho inside a 32-token block: lane group g = (rho/4)%2 of
+// the S^T output then holds tokens 16g .. 16g+15 in register order.
+__device__ __forceinline__ int perm_token(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
+
+// K row of token tok (D/2 bytes): chunk k is stored at k ^ kswz(tok).
+template <int D>
+__device__ __forceinline__ int kswz(int tok) {
+  if (D == 128) return (((tok >> 1) ^ (tok >> 2)) & 1) | (((tok >> 4) & 1) << 1);
+  return ((tok >> 1) ^ (tok >> 2) ^ (tok >> 4)) & 1;
+}
+// V record (block, channel) = 32 token bytes = 2 chunks: half h stored at h ^ vswz(ch).
+__device__ __forceinline__ int vswz(int ch) { return ((ch >> 2) ^ (ch >> 3)) & 1; }
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Streams the K/V tiles of one (batch, kv head) slice into LDS (NW waves
+// share the issue) with
+// buffer_load ... lds (no VGPR staging).  Each 1 KB (or 256 B) instruction
+// gets its own buffer resource, built with scalar arithmetic, that starts at
+// the instruction's bytes and covers only the slice's remaining valid bytes:
+// the hardware range check (on voffset + inst_offset) zero-fills a ragged last
+// tile and V blocks past the end, no read leaves the slice, and the per-lane
+// voffsets (which carry the LDS swizzle) stay loop-invariant, so issuing a
+// tile costs no VALU work.
+template <int D, int NW>
+struct TileLoader {
+  using TL = TileLayout<D>;
+  const uint8_t* kc;  // slice bases
+  const uint8_t* ks;
+  const uint8_t* vc;
+  const uint8_t* vs;
+  uint32_t kc_bytes, ks_bytes, vc_bytes, vs_bytes;  // valid bytes of each slice region
+  uint32_t vk0, vk1, vkw, vv;                        // per-lane voffsets (vkw: K codes, parity of `wave`)
+  int L;
+
+  // wave: index of the issuing wave when several waves split a tile (only its
+  // parity matters); 0 when one wave issues everything.
+  __device__ __forceinline__ void init(const uint8_t* k4, const uint8_t* k4s, const uint8_t* v8, const uint8_t* v8s,
+                                       size_t bg, int L_storage, int L_valid, int wave) {
+    const int nvb_storage = (L_storage + 31) / 32, nvb = (L_valid + 31) / 32;
+    L = L_valid;
+    kc = k4 + bg * L_storage * (D / 2);
+    ks = k4s + bg * L_storage * (D / 32);
+    vc = v8 + bg * nvb_storage * D * 32;
+    vs = v8s + bg * nvb_storage * D;
+    kc_bytes = (uint32_t)L_valid * (D / 2);
+    ks_bytes = (uint32_t)L_valid * (D / 32);
+    vc_bytes = (uint32_t)nvb * D * 32;
+    vs_bytes = (uint32_t)nvb * D;
+    const int p = threadIdx.x & 63;
+    if (D == 128) {  // 16 tokens of 64 B per KB; kswz uses token bits 1, 2 and 4 (= KB parity)
+      const int tl = p >> 2, kpos = p & 3;
+      vk0 = tl * 64 + 16 * (kpos ^ kswz<D>(tl));
+      vk1 = tl * 64 + 16 * (kpos ^ kswz<D>(tl + 16));
+    } else {         // 32 tokens of 32 B per KB
+      const int tl = p >> 1, kpos = p & 1;
+      vk0 = vk1 = tl * 32 + 16 * (kpos ^ kswz<D>(tl));
+    }
+    vkw = (wave & 1) ? vk1 : vk0;
+    const int rl = p >> 1, hpos = p & 1;  // 32 records of 32 B per KB; vswz uses record bits 2, 3
+    vv = rl * 32 + 16 * (hpos ^ vswz(rl));
+  }
+
+  // Resource for the bytes [off, ...) of a slice region.  A signed max has a
+  // scalar form (an unsigned saturating subtract would be VALU and make the
+  // descriptor divergent); both values are below 2^31.
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const uint8_t* base, uint32_t bytes, uint32_t off) {
+    const int rem = __builtin_amdgcn_readfirstlane(max((int)bytes - (int)off, 0));
+    // raw buffer (stride 0): voffset + inst_offset >= rem reads as zero
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + off), (short)0, rem, 0x00020000);
+  }
+
+  // Issue the K region (codes + scales) of tile t into kreg.  NW waves split
+  // the instructions: this wave issues indices wave, wave + NW, ...
+  __device__ __forceinline__ void issue_k(int t, uint8_t* kreg, int wave) const {
+    const int lane = threadIdx.x & 63;
+    constexpr int N = TL::NK + TL::NKS;
+#pragma unroll
+    for (int j = 0; j < (N + NW - 1) / NW; ++j) {
+      const int ins = wave + NW * j;
+      // (the descriptor is bound to a local: passing the call's result straight
+      // to the builtin loses the host launch stub of later kernel instances)
+      if (ins < TL::NK) {
+        const uint32_t voff = (NW % 2 == 0) ? vkw : ((ins & 1) ? vk1 : vk0);
+        const __amdgpu_buffer_rsrc_t r = rsrc_at(kc, kc_bytes, (uint32_t)t * TL::KC + ins * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(kreg + ins * 1024), 16, voff, 0, 0, 0);
+      } else if (ins < N) {
+        const int i = ins - TL::NK;
+        const __amdgpu_buffer_rsrc_t r = rsrc_at(ks, ks_bytes, (uint32_t)t * TL::KS_BYTES + i * 256);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(kreg + TL::KC + i * 256), 4, lane * 4, 0, 0, 0);
+      }
+    }
+  }
+  // Issue the V region (codes + scales) of tile t into vreg.
+  __device__ __forceinline__ void issue_v(int t, uint8_t* vreg, int wave) const {
+    const int lane = threadIdx.x & 63;
+    constexpr int N = TL::NV + 1;
+#pragma unroll
+    for (int j = 0; j < (N + NW - 1) / NW; ++j) {
+      const int ins = wave + NW * j;
+      if (ins < TL::NV) {
+        const __amdgpu_buffer_rsrc_t r = rsrc_at(vc, vc_bytes, (uint32_t)t * TL::VC + ins * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(vreg + ins * 1024), 16, vv, 0, 0, 0);
+      } else if (ins < N) {
+        const __amdgpu_buffer_rsrc_t r = rsrc_at(vs, vs_bytes, (uint32_t)t * TL::VS_BYTES);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(vreg + TL::VC), 16, lane * 16, 0, 0, 0);
+      }
+    }
+  }
+
+  // D = 64 with an odd key count: the last token's two scale bytes share a
+  // dword with bytes past the end, which the range check zeroes; patch them
+  // after the DMA has landed (called between the wait and the barrier).
+  __device__ __forceinline__ void fixup(int t, uint8_t* kreg) const {
+    if (D == 64 && (L & 1) && t == (L - 1) / kTile && (threadIdx.x & 63) == 0) {
+      const int j = (L - 1) - t * kTile;
+      kreg[TL::KC + 2 * j] = ks[2 * (L - 1)];
+      kreg[TL::KC + 2 * j + 1] = ks[2 * (L - 1) + 1];
+    }
+  }
+};
+
+// Channel-block assignment of the QK^T contraction.  MFMA k of a 32-key block
+// takes, in lane group g (lanes 32g .. 32g+31), the 32 channels of block
+// kblock(g, k): {2g, 2g+1} for D = 128, so a lane's two E8M0 bytes are
+// adjacent in a token's scale word (one 16-bit LDS read, picked by the
+// MFMA's byte select), and block g for D = 64.  Q uses the same assignment.
+template <int D>
+__device__ __forceinline__ int kblock(int g, int k) { return D == 128 ? 2 * g + k : g; }
+
+// Per-lane LDS byte offsets of a wave's operand reads, relative to a tile's K
+// or V region; the compile-time part of each address goes into the
+// instruction's offset field, so a read costs no VALU work.
+template <int D>
+struct LaneOffs {
+  uint32_t k[D / 64];  // K fragment of MFMA k; key block c adds 32c * D/2
+  uint32_t ks;         // K scale bytes (KC included); key block c adds 32c * D/32
+  uint32_t v;          // V fragment; (half h, part w, channel block cb) adds ((2h + w) * D + 32cb) * 32
+  uint32_t vs;         // V scale byte (VC included); adds 2h * D + 32cb
+
+  __device__ __forceinline__ void init() {
+    using TL = TileLayout<D>;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 5, rho = lane & 31;
+    const int tok = perm_token(rho);  // kswz depends on token bits 1, 2, 4 only: the same for every key block
+    const int sw = kswz<D>(tok);
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) this->k[k] = tok * (D / 2) + 16 * (kblock<D>(g, k) ^ sw);
+    ks = TL::KC + tok * (D / 32) + (D == 128 ? 2 * g : g);
+    v = rho * 32 + 16 * (g ^ vswz(rho));  // vswz depends on channel bits 2, 3 only
+    vs = TL::VC + g * D + rho;
+  }
+};
+
+// Per-wave state of 32 query rows.
+template <int D>
+struct RowState {
+  v4i qa[D / 64];  // Q fragments (B operand of S^T = K Q^T), channel blocks kblock(g, k)
+  int qs;          // their E8M0 scale bytes: byte k feeds MFMA k
+  v16f o[D / 32];  // O^T accumulators: o[cb][rr] = channel 32cb + (rr/4)*8 + 4g + rr%4
+  v16f lv;         // denominator 1 . P^T (every element equals the row sum), in the m_ref frame
+  float m;         // running max in log2 units, on the integer grid (-inf before any key)
+  float m_ref;     // frame of o and lv: both hold sum 2^(m_t - m_ref) P_t (V_t | 1)
+  v8i ones;        // FP8 1.0 in every byte: the A operand of the denominator product
+};
+
+// Softmax step of one tile: masks keys > jlim (when need_mask), moves the
+// running max m on the integer grid (log2 units), and converts
+// P = E4M3(256 * 2^(s*c2 + c2*delta - m)) into pb, the B operand of the P V
+// product (pb[h] covers keys 64h .. 64h+63).  pscale receives the E8M0 code of
+// 2^(m - m_ref) that the P V product applies.  O and l are touched only by the
+// rare frame rebase.
+template <int D>
+__device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int t, bool need_mask, int jlim, float c2,
+                                             float delta, v8i (&pb)[2], int& pscale) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  // ---- mask (diagonal / ragged tiles only); score s[c][rr] is key 128t + 32c + 16g + rr
+  if (need_mask) {
+    const int jb = kTile * t + 16 * g;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        if (jb + 32 * c + rr > jlim) s[c][rr] = -__builtin_inff();
+  }
+
+  // ---- row max (two left-associated chains: max(max(m, a), b) compiles to
+  // v_max3_f32, one instruction per two scores) and one lane swap
+  float mx0 = s[0][0], mx1 = s[2][0];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int rr = (c == 0 ? 1 : 0); rr < 16; rr += 2) {
+      if (rr + 1 < 16) {
+        mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s[c][rr]), s[c][rr + 1]);
+        mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[c + 2][rr]), s[c + 2][rr + 1]);
+      } else {
+        mx0 = __builtin_fmaxf(mx0, s[c][rr]);
+        mx1 = __builtin_fmaxf(mx1, s[c + 2][rr]);
+      }
+    }
+  float mx = __builtin_fmaxf(mx0, mx1);
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  // Running max on the integer grid: every rescale factor is an exact power of
+  // two, applied through the E8M0 scale of the P operand (no VALU work on O).
+  const float dlt = c2 * delta;
+  const float mt = __builtin_ceilf(__builtin_fmaf(mx, c2, dlt));
+  const float mn = __builtin_fmaxf(st.m, mt);
+  const float beta = (mn == -__builtin_inff()) ? 0.0f : dlt - mn;
+  if (st.m_ref == -__builtin_inff()) st.m_ref = mn;  // first visible key fixes the frame
+  st.m = mn;
+  // Keep 2^(m - m_ref) inside the E8M0 range: rebase the frame when it grows
+  // past 2^64 (rare: the row max would have to climb 64 binades).
+  if (__builtin_amdgcn_ballot_w64(mn - st.m_ref > 64.0f)) {
+    const float f = (mn - st.m_ref > 64.0f) ? __builtin_ldexpf(1.0f, (int)(st.m_ref - mn)) : 1.0f;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(st.o[cb][rr]) : "v"(f));
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(st.lv[rr]) : "v"(f));
+    if (mn - st.m_ref > 64.0f) st.m_ref = mn;
+  }
+  pscale = (mn == -__builtin_inff()) ? kScaleOne : kScaleOne + (int)(mn - st.m_ref);
+
+  // ---- P8 = E4M3(256 * 2^(s*c2 + beta)), packed as the B operand of O^T += V^T P^T
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = 2 * h + (k >> 2);
+      const int r0 = 4 * (k & 3);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r0 + 0], c2, beta));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r0 + 1], c2, beta));
+      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r0 + 2], c2, beta));
+      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r0 + 3], c2, beta));
+      // the old value of the destination is dead (both halves are written): reuse p0's register
+      v2s w = __builtin_bit_cast(v2s, p0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p0, p1, 0x1p-8f, false);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p2, p3, 0x1p-8f, true);
+      pb[h][k] = __builtin_bit_cast(int, w);
+    }
+}
+
+// One K operand block (32 keys x all channels): the A operands of the D/64
+// MFMAs of key block c and their scale bytes (byte k feeds MFMA k).
+template <int D>
+struct KBlk {
+  v4i ka[D / 64];
+  int sc;
+};
+
+template <int D>
+__device__ __forceinline__ void load_k_blk(const uint8_t* kreg, const LaneOffs<D>& lo, int c, KBlk<D>& k) {
+#pragma unroll
+  for (int kk = 0; kk < D / 64; ++kk)
+    k.ka[kk] = *reinterpret_cast<const v4i*>(kreg + lo.k[kk] + 32 * c * (D / 2));
+  if (D == 128)
+    k.sc = *reinterpret_cast<const uint16_t*>(kreg + lo.ks + 32 * c * (D / 32));
+  else
+    k.sc = kreg[lo.ks + 32 * c * (D / 32)];
+}
+
+// S^T block c = K_c Q^T: sc_[rr] is the score of this lane's row (l % 32)
+// against key 32c + 16g + rr of the tile (g = l / 32).
+template <int D>
+__device__ __forceinline__ void qk_blk(const RowState<D>& st, const KBlk<D>& k, v16f& sc_) {
+  sc_ = v16f{};
+  sc_ = mfma_fp4_32x32x64_sel<0>(k.ka[0], st.qa[0], sc_, k.sc, st.qs);
+  if (D == 128) sc_ = mfma_fp4_32x32x64_sel<1>(k.ka[D / 64 - 1], st.qa[D / 64 - 1], sc_, k.sc, st.qs);
+}
+
+// One V operand (64 keys x 32 channels: half h = q / (D/32), channel block
+// cb = q % (D/32)) and its E8M0 scale byte.
+template <int D>
+__device__ __forceinline__ void load_v_op(const uint8_t* vreg, const LaneOffs<D>& lo, int q, v8i& a, int& sa) {
+  const int h = q / (D / 32), cb = q % (D / 32);
+  const v4i a0 = *reinterpret_cast<const v4i*>(vreg + lo.v + ((2 * h) * D + 32 * cb) * 32);
+  const v4i a1 = *reinterpret_cast<const v4i*>(vreg + lo.v + ((2 * h + 1) * D + 32 * cb) * 32);
+  a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  sa = vreg[lo.vs + 2 * h * D + 32 * cb];
+}
+
+// O^T += 2^(m - m_ref) V^T P^T of one tile (FP8 x FP8; V's E8M0 scale per 32
+// tokens x channel, P's per row) and the denominator, the same product
+// against ones, followed by S = K Q^T of the next tile.  Software-pipelined
+// over a small ring of operand registers: V operands are read three products
+// ahead and the first two K blocks during the last P V products, so the MFMAs
+// issue back to back while LDS reads stay in flight.  The scheduler fences
+// keep this order within the register budget of two waves per SIMD.
+template <int D>
+__device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D>& lo, const uint8_t* vreg,
+                                           const v8i (&pb)[2], int pscale, const uint8_t* kreg, v16f (&s)[4]) {
+  constexpr int NQ = 2 * (D / 32);  // P V products (excluding the denominator)
+  constexpr int R = 3;              // V operands in flight
+  v8i va[R];
+  int vs[R];
+  KBlk<D> kb[2];
+#pragma unroll
+  for (int q = 0; q < R; ++q) load_v_op<D>(vreg, lo, q, va[q], vs[q]);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int h = q / (D / 32), cb = q % (D / 32);
+    st.o[cb] = mfma_fp8_32x32x64(va[q % R], pb[h], st.o[cb], vs[q % R], pscale);
+    if (cb == D / 32 - 1) st.lv = mfma_fp8_32x32x64(st.ones, pb[h], st.lv, kScaleOne, pscale);
+    if (q + R < NQ)
+      load_v_op<D>(vreg, lo, q + R, va[q % R], vs[q % R]);
+    else if (q + R - NQ < 2)
+      load_k_blk<D>(kreg, lo, q + R - NQ, kb[q + R - NQ]);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    __builtin_amdgcn_sched_barrier(0);
+    qk_blk<D>(st, kb[c & 1], s[c]);
+    if (c + 2 < 4) load_k_blk<D>(kreg, lo, c + 2, kb[c & 1]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// P V of one tile alone, pipelined like pv_then_qk.
+template <int D>
+__device__ __forceinline__ void pv_tile(RowState<D>& st, const LaneOffs<D>& lo, const uint8_t* vreg,
+                                        const v8i (&pb)[2], int pscale) {
+  constexpr int NQ = 2 * (D / 32);
+  constexpr int R = 3;
+  v8i va[R];
+  int vs[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) load_v_op<D>(vreg, lo, q, va[q], vs[q]);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int h = q / (D / 32), cb = q % (D / 32);
+    st.o[cb] = mfma_fp8_32x32x64(va[q % R], pb[h], st.o[cb], vs[q % R], pscale);
+    if (cb == D / 32 - 1) st.lv = mfma_fp8_32x32x64(st.ones, pb[h], st.lv, kScaleOne, pscale);
+    if (q + R < NQ) load_v_op<D>(vreg, lo, q + R, va[q % R], vs[q % R]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// S = K Q^T of one tile alone, two K blocks in flight.
+template <int D>
+__device__ __forceinline__ void qk_tile(const RowState<D>& st, const LaneOffs<D>& lo, const uint8_t* kreg,
+                                        v16f (&s)[4]) {
+  KBlk<D> kb[2];
+  load_k_blk<D>(kreg, lo, 0, kb[0]);
+  load_k_blk<D>(kreg, lo, 1, kb[1]);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    __builtin_amdgcn_sched_barrier(0);
+    qk_blk<D>(st, kb[c & 1], s[c]);
+    if (c + 2 < 4) load_k_blk<D>(kreg, lo, c + 2, kb[c & 1]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Epilogue of one row: O = O^T / l (this lane writes half of the row's
+// channels) and LSE = ln2 * (m_ref + log2(l / 256)).  lse_row may be null.
+template <int D>
+__device__ __forceinline__ void store_row(const RowState<D>& st, float* orow, float* lse_row) {
+  const int g = (threadIdx.x & 63) >> 5;
+  const float l = st.lv[0];
+  const bool empty = (st.m == -__builtin_inff());
+  const float inv = empty ? 0.0f : 1.0f / l;
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) orow[32 * cb + (rr >> 2) * 8 + 4 * g + (rr & 3)] = st.o[cb][rr] * inv;
+  if (lse_row && g == 0)
+    *lse_row = empty ? -__builtin_inff() : 0.69314718055994531f * (st.m_ref + __builtin_log2f(l * 0x1p-8f));
+}
+
+// delta^T for 32 tiles starting at tau0: Kbar[tau0 .. tau0+31] . Q_bf16^T,
+// into the wave's LDS slab dl[tile][row] as binary32.  The products of two bf16
+// values are exact in binary64 and a sum of D of them stays exact there, so the
+// FP64 MFMA (v_mfma_f64_16x16x4f64) yields the exactly rounded binary32 value:
+// the per-(row, tile) exponent offset, which decides P codes, is then the same
+// number the binary64 definition gives.  Four 16x16 blocks (2 tile halves x 2
+// row halves); the contraction index of step s, lane group g is channel
+// 32 g + s (any pairing works as long as A and B agree).
+template <int D>
+__device__ __forceinline__ void compute_delta(float* dl, const uint16_t* kbar_bg, int ntk, int tau0,
+                                              const uint16_t* qbase, int q_stride, int nrows_valid) {
+  typedef double v4d __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  constexpr int CPG = D / 4;  // channels per lane group
+  // one 16 x 16 block (tile half tb, row half rb) at a time: few live registers
+#pragma unroll 1
+  for (int blk = 0; blk < 4; ++blk) {
+    const int tb = blk >> 1, rb = blk & 1;
+    const int tau = tau0 + 16 * tb + r16, row = 16 * rb + r16;
+    v4d acc = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s8 = 0; s8 < CPG; s8 += 8) {
+      const int c0 = CPG * g + s8;
+      uint4 ka = {0u, 0u, 0u, 0u}, qa = {0u, 0u, 0u, 0u};
+      if (tau < ntk) ka = *reinterpret_cast<const uint4*>(kbar_bg + (size_t)tau * D + c0);
+      if (row < nrows_valid) qa = *reinterpret_cast<const uint4*>(qbase + (size_t)row * q_stride + c0);
+      const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w}, qaw[4] = {qa.x, qa.y, qa.z, qa.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) ? 16 : 0;
+        const double A = (double)bf16_bits_to_float((kaw[e >> 1] >> sh) & 0xFFFFu);
+        const double B = (double)bf16_bits_to_float((qaw[e >> 1] >> sh) & 0xFFFFu);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(A, B, acc, 0, 0, 0);
+      }
+    }
+    // FP64 16x16 result layout: register r of lane l holds entry (i, j) = (l / 16 + 4 r, l % 16):
+    // tile 16 tb + lane / 16 + 4 r, query row 16 rb + lane % 16
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dl[(16 * tb + g + 4 * r) * 32 + 16 * rb + r16] = (float)acc[r];
+  }
+}
+
+// Q fragments of this lane's row (zeros when invalid) and a fresh row state.
+template <int D>
+__device__ __forceinline__ void load_q(RowState<D>& st, const uint8_t* q4row, const uint8_t* q4srow, bool valid) {
+  const int g = (threadIdx.x & 63) >> 5;
+  st.qs = 0;
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) {
+    const int b = kblock<D>(g, k);
+    st.qa[k] = valid ? *reinterpret_cast<const v4i*>(q4row + 16 * b) : v4i{0, 0, 0, 0};
+    st.qs |= (valid ? (int)q4srow[b] : 0) << (8 * k);
+  }
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) st.o[cb] = v16f{};
+  st.lv = v16f{};
+  st.m = -__builtin_inff();
+  st.m_ref = -__builtin_inff();
+  st.ones = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  asm volatile("" : "+v"(st.ones));  // resident in VGPRs for the whole loop (no per-tile rebuild)
+}
+
+}  // namespace qfa

@@ -52,6 +52,14 @@ __device__ __forceinline__ v16f mfma_fp4_32x32x64(v4i a, v4i b, v16f c, int sa, 
   v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
 }
+// E2M1 x E2M1 with the scale byte SEL (0..3) of sa and sb selected by the
+// instruction's byte select.
+template <int SEL>
+__device__ __forceinline__ v16f mfma_fp4_32x32x64_sel(v4i a, v4i b, v16f c, int sa, int sb) {
+  v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, SEL, sa, SEL, sb);
+}
 __device__ __forceinline__ v16f mfma_fp8_32x32x64(v8i a, v8i b, v16f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
