@@ -224,14 +224,21 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
                                              float delta, v8i (&pb)[2], int& pscale) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
-  // ---- mask (diagonal / ragged tiles only); score s[c][rr] is key 128t + 32c + 16g + rr
+  // ---- mask (diagonal / ragged tiles only); score s[c][rr] is key 128t + 32c + 16g + rr.
+  // A lane's 16 keys of block c are consecutive, so the visible ones are a
+  // prefix rr <= nvm1; the select is done on the bits ((nvm1 - rr) >> 31 is -1
+  // for a masked key), which keeps 64 comparison masks out of the SGPRs.
   if (need_mask) {
     const int jb = kTile * t + 16 * g;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 4; ++c) {
+      const int nvm1 = jlim - (jb + 32 * c);
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr)
-        if (jb + 32 * c + rr > jlim) s[c][rr] = -__builtin_inff();
+      for (int rr = 0; rr < 16; ++rr) {
+        const int msk = (nvm1 - rr) >> 31;
+        s[c][rr] = __int_as_float((__float_as_int(s[c][rr]) & ~msk) | (int)(0xFF800000u & (uint32_t)msk));
+      }
+    }
   }
 
   // ---- row max (two left-associated chains: max(max(m, a), b) compiles to
