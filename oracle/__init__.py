@@ -73,7 +73,7 @@ def lib():
         L.orc_bf16_from_double.restype = ctypes.c_uint16
         L.orc_bf16_from_double.argtypes = [D]
         L.orc_quantize_qk4.restype = None
-        L.orc_quantize_qk4.argtypes = [P, I64, I64, I64, I64, I, P, P, P]
+        L.orc_quantize_qk4.argtypes = [P, I64, I64, I64, I64, I, F, P, P, P]
         L.orc_quantize_v8.restype = None
         L.orc_quantize_v8.argtypes = [P, I64, I64, I64, I64, P, P]
         L.orc_dequant_qk4.restype = None
@@ -164,16 +164,27 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------- quantizers
-def quantize_qk4(x_bits: np.ndarray, smooth: bool = False):
+LOG2E_F32 = np.float32(1.44269502162933349609375)
+
+
+def exp2_scale(softmax_scale: float) -> float:
+    """c2 = fl32(softmax_scale * log2 e): the factor Q is multiplied by before
+    it is quantised, so that Q'K^T is the exponent argument in log2 units."""
+    return float(np.float32(softmax_scale) * LOG2E_F32)
+
+
+def quantize_qk4(x_bits: np.ndarray, smooth: bool = False, prescale: float = 1.0):
     """x [B,H,S,D] bf16 bits -> (codes [B,H,S,D/2] u8, scales [B,H,S,D/32] u8,
-    kbar [B,H,ceil(S/128),D] bf16 bits or None)."""
+    kbar [B,H,ceil(S/128),D] bf16 bits or None).  Elements are multiplied by
+    prescale in binary32 before quantisation (Q: exp2_scale(softmax_scale))."""
     x = _c(x_bits, np.uint16)
     B, H, S, D = x.shape
     codes = np.empty((B, H, S, D // 2), np.uint8)
     scales = np.empty((B, H, S, D // BLOCK), np.uint8)
     nt = (S + TILE - 1) // TILE
     kbar = np.empty((B, H, nt, D), np.uint16) if smooth else None
-    lib().orc_quantize_qk4(_p(x), B, H, S, D, int(bool(smooth)), _p(codes), _p(scales), _p(kbar))
+    lib().orc_quantize_qk4(_p(x), B, H, S, D, int(bool(smooth)), float(np.float32(prescale)), _p(codes),
+                           _p(scales), _p(kbar))
     return codes, scales, kbar
 
 
@@ -226,7 +237,9 @@ def attn_exact_rows(Q, qpos, K, V, Sq, causal, softmax_scale):
 
 def attn_quant_rows(Q, qpos, K, V, Sq, causal, softmax_scale, Qc=None, Kbar=None, split_tiles=0,
                     quantize_p=True, fp32_arg=True):
-    """(c) the method's online-softmax schedule for rows Q [n,D] of one kv head."""
+    """(c) the method's online-softmax schedule for rows Q [n,D] of one kv head.
+    Q holds pre-scaled query rows q' = c2 q (see exp2_scale), so Q K^T is in
+    log2 units; softmax_scale still enters the compensation term."""
     Q = _c(Q, np.float64)
     K = _c(K, np.float64)
     V = _c(V, np.float64)
@@ -286,7 +299,7 @@ def prefill_rows(q_bits, k_bits, v_bits, rows: Sequence, causal: bool, softmax_s
         for h in np.unique(r[:, 1]):
             sel = np.nonzero(r[:, 1] == h)[0]
             qh = np.ascontiguousarray(q_bits[b:b + 1, h:h + 1])
-            qc_, qs_, _ = quantize_qk4(qh)
+            qc_, qs_, _ = quantize_qk4(qh, prescale=exp2_scale(softmax_scale))
             qd = dequant_qk4(qc_, qs_)[0, 0]
             Qd[sel] = qd[r[sel, 2]]
             Qc[sel] = bf16_to_f64(q_bits[b, h][r[sel, 2]])
@@ -333,7 +346,8 @@ def decode_rows(q_bits, k_bits, v_bits, rows: Sequence, softmax_scale: float, nu
         Vd = dequant_v8(vc[0, 0], vs[0, 0], L)
         Qd = np.zeros((len(idx), D))
         for j, (bb, h, _) in enumerate(r):
-            qc_, qs_, _ = quantize_qk4(np.ascontiguousarray(q_bits[bb:bb + 1, h:h + 1]))
+            qc_, qs_, _ = quantize_qk4(np.ascontiguousarray(q_bits[bb:bb + 1, h:h + 1]),
+                                       prescale=exp2_scale(softmax_scale))
             Qd[j] = dequant_qk4(qc_, qs_)[0, 0, 0]
         O, lse = attn_quant_rows(Qd, np.zeros(len(idx), np.int64), Kd, Vd, 1, False, softmax_scale,
                                  split_tiles=per)

@@ -39,6 +39,11 @@
  *  - Element rounding: round-to-nearest, ties to the even code, applied once to
  *    the exact value x * 2^-e; the sign of zero is kept; magnitudes beyond the
  *    largest finite value saturate to it.
+ *  - Softmax scale: S = Q K^T / sqrt(d) is exponentiated in base 2, so the
+ *    factor c2 = fl32(softmax_scale * log2 e) is applied to Q before Q is
+ *    quantised (Q' = fl32(q * c2), then MXFP4).  The pages do not say where
+ *    the scale enters; applied to Q, the product Q'K^T is already the
+ *    exponent argument in log2 units.
  *  - P is E4M3(256 * 2^(s - m)) with m the running max in log2 units kept on
  *    the integer grid: after every 128-token key tile (ascending order)
  *    m <- max(m, ceil(max_j s_j)).  Online softmax only needs m to bound the
@@ -56,8 +61,10 @@
  *  - Decode splits are contiguous runs of whole 128-token tiles, merged by
  *    log-sum-exp.
  *  - The exponent argument of P (which decides an integer code) is formed in
- *    binary32 in the order the GPU kernel forms it (fp32_arg = 1); every
- *    exponential, sum and product is still evaluated in binary64.
+ *    binary32 as the kernel forms it (fp32_arg = 1):
+ *    y = fl32(fl32(S) + fl32(c2 * fl32(delta))), m' = max(m, ceil(max y)),
+ *    P = E4M3(256 * 2^(y - m')).  Without the compensation y = S exactly.
+ *    Every exponential, sum and product is still evaluated in binary64.
  */
 #include <math.h>
 #include <stdint.h>
@@ -226,8 +233,12 @@ static int mxfp4_block(const double* x, uint8_t* codes) {
 /* Q or K [B][H][S][D] bf16 -> codes [B][H][S][D/2], scales [B][H][S][D/32].
  * With smooth != 0 the 128-token channel means are written to kbar
  * [B][H][ceil(S/128)][D] and the quantised tensor is fl32(K - Kbar) (one
- * correctly rounded binary32 subtraction).  D must be a multiple of 32. */
-void orc_quantize_qk4(const uint16_t* x, int64_t B, int64_t H, int64_t S, int64_t D, int smooth,
+ * correctly rounded binary32 subtraction).  Each element is then multiplied
+ * by prescale in binary32 (fl32(v * prescale); 1 leaves it unchanged): Q is
+ * quantised as fl32(q * c2) with c2 = fl32(softmax_scale * log2 e), so that
+ * Q'K^T is already the exponent argument in log2 units.  D must be a
+ * multiple of 32. */
+void orc_quantize_qk4(const uint16_t* x, int64_t B, int64_t H, int64_t S, int64_t D, int smooth, float prescale,
                       uint8_t* codes, uint8_t* scales, uint16_t* kbar) {
   int64_t nt = (S + QFA_ORC_TILE - 1) / QFA_ORC_TILE;
   int64_t nb = D / QFA_ORC_BLOCK;
@@ -243,6 +254,7 @@ void orc_quantize_qk4(const uint16_t* x, int64_t B, int64_t H, int64_t S, int64_
           int64_t c = blk * QFA_ORC_BLOCK + i;
           double v = orc_bf16_value(xs[s * D + c]);
           if (smooth) v = (double)(float)(v - orc_bf16_value(kb[(s / QFA_ORC_TILE) * D + c]));
+          if (prescale != 1.0f) v = (double)((float)v * prescale);
           buf[i] = v;
         }
         int64_t row = bh * S + s;
@@ -365,9 +377,10 @@ void orc_attn_exact_rows(const double* Q, const int64_t* qpos, int64_t n, const 
 
 #define LOG2E_F32 1.44269502162933349609375f /* binary32 nearest to log2(e) */
 
-/* One split [t0, t1) of 128-token tiles for one query row.  Returns 0 if no key
- * of the split is visible (the split then has weight 0), else fills o (already
- * divided by l) and *lse_out. */
+/* One split [t0, t1) of 128-token tiles for one query row.  q is the
+ * pre-scaled query row (q' = c2 q, so q' . k is in log2 units).  Returns 0 if
+ * no key of the split is visible (the split then has weight 0), else fills o
+ * (already divided by l) and *lse_out. */
 static int split_row(const double* q, const double* qc, int64_t i, const double* K, const double* Kbar,
                      const double* V, int64_t L, int64_t Sq, int64_t D, int causal, float scale32,
                      int64_t t0, int64_t t1, int quantize_p, int fp32_arg, double* o, double* lse_out,
@@ -380,7 +393,7 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
   for (int64_t t = t0; t < t1; ++t) {
     int64_t j0 = t * QFA_ORC_TILE, j1 = j0 + QFA_ORC_TILE < L ? j0 + QFA_ORC_TILE : L;
     if (j0 >= L) break;
-    /* logits of the tile (exact); masked keys marked with -inf */
+    /* logits of the tile in log2 units (exact); masked keys marked with -inf */
     double smax = -INFINITY;
     for (int64_t j = j0; j < j1; ++j) {
       if (!visible(i, j, L, Sq, causal)) {
@@ -400,26 +413,30 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
       for (int64_t c = 0; c < D; ++c) delta += qc[c] * Kbar[t * D + c];
     double mnew, alpha;
     if (fp32_arg) {
-      /* exponent argument in binary32: t_j = fma(S_j, c2, beta) with
-       * delta32 = fl32(c2 * fl32(delta)), m_tile = fma(max S, c2, delta32),
-       * beta = fl32(delta32 - m') */
-      float d32 = c2f * (float)delta;
-      float mt = ceilf(fmaf((float)smax, c2f, d32));
-      float mn = (m == -INFINITY || mt > (float)m) ? mt : (float)m;
-      float beta = d32 - mn;
-      alpha = (m == -INFINITY) ? 0.0 : exp2(m - (double)mn);
-      mnew = mn;
+      /* Exponent argument in binary32, as the kernel forms it:
+       *   y_j = fl32(fl32(S_j) + delta32),  delta32 = fl32(c2 * fl32(delta)),
+       *   m' = max(m, ceil(max_j y_j)),  P_j = E4M3(256 * 2^(y_j - m')). */
+      const float d32 = Kbar ? c2f * (float)delta : 0.0f;
+      float ymax = -INFINITY;
+      for (int64_t j = 0; j < j1 - j0; ++j) {
+        if (S[j] == -INFINITY) continue;
+        float y = (float)S[j] + d32;
+        S[j] = (double)y; /* from here S holds y */
+        if (y > ymax) ymax = y;
+      }
+      const double mt = ceil((double)ymax);
+      mnew = (m == -INFINITY || mt > m) ? mt : m;
+      alpha = (m == -INFINITY) ? 0.0 : exp2(m - mnew);
       for (int64_t j = 0; j < j1 - j0; ++j) {
         if (S[j] == -INFINITY) {
           P[j] = 0.0;
           continue;
         }
-        float targ = fmaf((float)S[j], c2f, beta);
-        double p = ldexp(exp2((double)targ), 8);
+        double p = ldexp(exp2(S[j] - mnew), 8);
         P[j] = quantize_p ? orc_e4m3_value(orc_e4m3_encode(p)) : p;
       }
     } else {
-      double mt = ceil(c2d * (smax + delta));
+      double mt = ceil(smax + c2d * delta);
       mnew = (mt > m) ? mt : m;
       alpha = (m == -INFINITY) ? 0.0 : exp2(m - mnew);
       for (int64_t j = 0; j < j1 - j0; ++j) {
@@ -427,7 +444,7 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
           P[j] = 0.0;
           continue;
         }
-        double p = ldexp(exp2(c2d * (S[j] + delta) - mnew), 8);
+        double p = ldexp(exp2(S[j] + c2d * delta - mnew), 8);
         P[j] = quantize_p ? orc_e4m3_value(orc_e4m3_encode(p)) : p;
       }
     }
@@ -452,13 +469,16 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
 
 /*
  * Quantised attention for n query rows of one (batch, kv head):
- *   Q  [n][D]   query rows (decoded MXFP4, or raw values for the identity path)
+ *   Q  [n][D]   pre-scaled query rows q' = c2 q (decoded MXFP4 of fl32(q c2),
+ *               or exact values for the identity path), so q' . k is the
+ *               logit in log2 units
  *   Qc [n][D]   bf16 query rows for the compensation term, or NULL
  *   qpos[n]     query index i in [0, Sq)
  *   K, V [L][D] keys and values (decoded), Kbar [ceil(L/128)][D] or NULL
  *   split_tiles 0: one split over all tiles; else tiles per decode split
  *   quantize_p  1: P rounded to E4M3; 0: identity quantiser (exact P)
- *   fp32_arg    1: exponent argument formed in binary32 (see header)
+ *   fp32_arg    1: exponent argument formed in binary32 (see split_row);
+ *               0: everything in binary64
  * Outputs O [n][D], lse [n].  Rows with no visible key get O = 0, lse = -inf.
  */
 void orc_attn_quant_rows(const double* Q, const double* Qc, const int64_t* qpos, int64_t n, const double* K,

@@ -5,6 +5,10 @@ torch's float64 softmax (an independent library) with bottom-right causal masks
 and GQA; (c)'s quantised path is checked with closed-form special cases,
 invariants, and a brute-force recomputation of tiny inputs that uses torch's
 float8 rounding instead of the oracle's encoder.
+
+(c) takes pre-scaled query rows q' = c2 q (c2 = softmax_scale * log2 e), so
+q' . k is the logit in log2 units; the exact references below multiply by c2
+in binary64 before calling it.
 """
 import math
 
@@ -13,6 +17,12 @@ import pytest
 import torch
 
 import oracle
+
+
+def c2d(scale):
+    """softmax_scale * log2 e in binary64, with the scale rounded to binary32 as
+    the oracle receives it."""
+    return float(np.float32(scale)) * math.log2(math.e)
 
 
 def torch_attention(Q, K, V, Sq, causal, scale, qpos):
@@ -59,8 +69,8 @@ def test_online_schedule_identity_quantizer_equals_softmax(L, Sq, causal, split)
     K = rng.standard_normal((L, D))
     V = rng.standard_normal((L, D))
     qpos = np.arange(Sq)
-    O, lse = oracle.attn_quant_rows(Q, qpos, K, V, Sq, causal, 0.125, split_tiles=split, quantize_p=False,
-                                    fp32_arg=False)
+    O, lse = oracle.attn_quant_rows(Q * c2d(0.125), qpos, K, V, Sq, causal, 0.125, split_tiles=split,
+                                    quantize_p=False, fp32_arg=False)
     Or, lr = torch_attention(Q, K, V, Sq, causal, float(np.float32(0.125)), qpos)
     assert np.abs(O - Or).max() < 1e-12
     assert np.abs(lse - lr).max() < 1e-11
@@ -79,23 +89,25 @@ def test_compensation_identity_restores_logits():
     Kbar = np.stack([K[t * 128:(t + 1) * 128].mean(axis=0) for t in range(nt)])
     Ks = K - np.repeat(Kbar, 128, axis=0)[:L]
     qpos = np.arange(Sq)
-    O, lse = oracle.attn_quant_rows(Q, qpos, Ks, V, Sq, True, 0.125, Qc=Q, Kbar=Kbar, quantize_p=False,
-                                    fp32_arg=False)
+    O, lse = oracle.attn_quant_rows(Q * c2d(0.125), qpos, Ks, V, Sq, True, 0.125, Qc=Q, Kbar=Kbar,
+                                    quantize_p=False, fp32_arg=False)
     Or, lr = torch_attention(Q, K, V, Sq, True, float(np.float32(0.125)), qpos)
     assert np.abs(O - Or).max() < 1e-10
     assert np.abs(lse - lr).max() < 1e-10
     # without the compensation term the result is different (the term matters)
-    O2, _ = oracle.attn_quant_rows(Q, qpos, Ks, V, Sq, True, 0.125, quantize_p=False, fp32_arg=False)
+    O2, _ = oracle.attn_quant_rows(Q * c2d(0.125), qpos, Ks, V, Sq, True, 0.125, quantize_p=False,
+                                   fp32_arg=False)
     assert np.abs(O2 - Or).max() > 1e-3
 
 
-def _quantized_inputs(rng, Sq, L, D, scale_q=1.0):
+def _quantized_inputs(rng, Sq, L, D, scale_q=1.0, softmax_scale=0.125):
+    """Decoded Q' (quantised as fl32(q * c2)), K and V of random bf16 inputs."""
     def bf(x):
         return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     q = bf(rng.standard_normal((1, 1, Sq, D)) * scale_q)
     k = bf(rng.standard_normal((1, 1, L, D)))
     v = bf(rng.standard_normal((1, 1, L, D)))
-    qc, qs, _ = oracle.quantize_qk4(q)
+    qc, qs, _ = oracle.quantize_qk4(q, prescale=oracle.exp2_scale(softmax_scale))
     kc, ks, _ = oracle.quantize_qk4(k)
     vc, vs = oracle.quantize_v8(v)
     return (oracle.dequant_qk4(qc, qs)[0, 0], oracle.dequant_qk4(kc, ks)[0, 0],
@@ -115,7 +127,7 @@ def test_single_tile_equals_two_pass_definition():
     Qd, Kd, Vd = _quantized_inputs(rng, Sq, L, D, scale_q=3.0)
     scale = float(np.float32(0.125))
     O, lse = oracle.attn_quant_rows(Qd, np.arange(Sq), Kd, Vd, Sq, False, scale, fp32_arg=False)
-    s = (Qd @ Kd.T) * scale * math.log2(math.e)
+    s = Qd @ Kd.T  # log2 units (Q' carries the scale)
     m = np.ceil(s.max(axis=1, keepdims=True))
     p = _e4m3_torch(256.0 * np.exp2(s - m))
     Oref = (p @ Vd) / p.sum(axis=1, keepdims=True)
@@ -134,7 +146,7 @@ def test_two_tiles_online_schedule_bruteforce():
     Qd, Kd, Vd = _quantized_inputs(rng, Sq, L, D, scale_q=3.0)
     scale = float(np.float32(0.125))
     O, _ = oracle.attn_quant_rows(Qd, np.arange(Sq), Kd, Vd, Sq, False, scale, fp32_arg=False)
-    s = (Qd @ Kd.T) * scale * math.log2(math.e)
+    s = Qd @ Kd.T  # log2 units
     s1, s2 = s[:, :128], s[:, 128:]
     m1 = np.ceil(s1.max(axis=1, keepdims=True))
     m2 = np.maximum(m1, np.ceil(s2.max(axis=1, keepdims=True)))
@@ -213,8 +225,8 @@ def test_no_visible_key_and_empty_splits():
     Q1 = rng.standard_normal((1, D))
     K1 = rng.standard_normal((300, D))
     V1 = rng.standard_normal((300, D))
-    Oa, la = oracle.attn_quant_rows(Q1, np.zeros(1, np.int64), K1, V1, 1, False, 0.125, split_tiles=2,
-                                    quantize_p=False, fp32_arg=False)
+    Oa, la = oracle.attn_quant_rows(Q1 * c2d(0.125), np.zeros(1, np.int64), K1, V1, 1, False, 0.125,
+                                    split_tiles=2, quantize_p=False, fp32_arg=False)
     Or, lr = torch_attention(Q1, K1, V1, 1, False, float(np.float32(0.125)), [0])
     assert np.abs(Oa - Or).max() < 1e-12 and abs(la[0] - lr[0]) < 1e-12
 
@@ -224,8 +236,8 @@ def test_fp32_argument_close_to_fp64_argument():
     rounding boundary; O stays within 1e-5 of the binary64-argument result."""
     rng = np.random.default_rng(43)
     Sq, L, D = 64, 700, 128
-    Qd, Kd, Vd = _quantized_inputs(rng, Sq, L, D, scale_q=2.0)
     scale = 1 / math.sqrt(128)
+    Qd, Kd, Vd = _quantized_inputs(rng, Sq, L, D, scale_q=2.0, softmax_scale=scale)
     Oa, la = oracle.attn_quant_rows(Qd, np.arange(Sq), Kd, Vd, Sq, True, scale, fp32_arg=True)
     Ob, lb = oracle.attn_quant_rows(Qd, np.arange(Sq), Kd, Vd, Sq, True, scale, fp32_arg=False)
     assert np.abs(Oa - Ob).max() < 1e-5
@@ -264,12 +276,36 @@ def test_split_schedule_invariance_on_integer_grid(fp32_arg):
     the single-split codes except in E4M3's subnormal range (~1e-5 effect)."""
     rng = np.random.default_rng(53)
     L, D = 2000, 128
-    Qd, Kd, Vd = _quantized_inputs(rng, 4, L, D, scale_q=2.0)
     scale = 1 / math.sqrt(128)
+    Qd, Kd, Vd = _quantized_inputs(rng, 4, L, D, scale_q=2.0, softmax_scale=scale)
     O1, l1 = oracle.attn_quant_rows(Qd, np.zeros(4, np.int64), Kd, Vd, 1, False, scale, split_tiles=0,
                                     fp32_arg=fp32_arg)
     for per in (1, 3, 7):
         Os, ls = oracle.attn_quant_rows(Qd, np.zeros(4, np.int64), Kd, Vd, 1, False, scale, split_tiles=per,
                                         fp32_arg=fp32_arg)
+        assert np.abs(Os - O1).max() < 1e-4
+        assert np.abs(ls - l1).max() < 1e-4
+
+
+def test_fp32_argument_with_compensation_close_to_fp64():
+    """With the compensation the binary32 argument fl32(S + delta32) rounds;
+    that only moves rare codes across a rounding boundary: O within 1e-5 of
+    the binary64 path, and split schedules agree to 1e-4."""
+    rng = np.random.default_rng(59)
+    Sq, L, D = 32, 900, 128
+    scale = 1 / math.sqrt(128)
+    Qd, Kd, Vd = _quantized_inputs(rng, Sq, L, D, scale_q=2.0, softmax_scale=scale)
+    nt = (L + 127) // 128
+    Qc = rng.standard_normal((Sq, D))
+    Kbar = rng.normal(0, 3, (nt, D))
+    Oa, la = oracle.attn_quant_rows(Qd, np.arange(Sq), Kd, Vd, Sq, True, scale, Qc=Qc, Kbar=Kbar, fp32_arg=True)
+    Ob, lb = oracle.attn_quant_rows(Qd, np.arange(Sq), Kd, Vd, Sq, True, scale, Qc=Qc, Kbar=Kbar, fp32_arg=False)
+    assert np.abs(Oa - Ob).max() < 1e-5
+    assert np.abs(la - lb).max() < 1e-5
+    Q1 = Qd[:2]
+    O1, l1 = oracle.attn_quant_rows(Q1, np.zeros(2, np.int64), Kd, Vd, 1, False, scale, Qc=Qc[:2], Kbar=Kbar)
+    for per in (1, 3):
+        Os, ls = oracle.attn_quant_rows(Q1, np.zeros(2, np.int64), Kd, Vd, 1, False, scale, Qc=Qc[:2], Kbar=Kbar,
+                                        split_tiles=per)
         assert np.abs(Os - O1).max() < 1e-4
         assert np.abs(ls - l1).max() < 1e-4

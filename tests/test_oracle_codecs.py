@@ -175,6 +175,35 @@ def test_mxfp4_quantizer_bruteforce():
     assert ((blocks[nz] > 1.5) & (blocks[nz] <= 4.0)).all()
 
 
+def test_mxfp4_prescaled_quantizer_bruteforce():
+    """Q is quantised as fl32(q * c2): the binary32 product (numpy float32
+    multiply) is brute-forced through the block rule and the printed E2M1
+    table; a power-of-two prescale only moves the scale byte."""
+    table = gold("e2m1_magnitudes.json")["magnitudes"]
+    rng = np.random.default_rng(13)
+    B, H, S, D = 1, 1, 23, 64
+    x = rng.standard_normal((B, H, S, D)).astype(np.float32) * 3.0
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    c2 = oracle.exp2_scale(1.0 / math.sqrt(128))
+    assert c2 == float(np.float32(np.float32(1.0 / math.sqrt(128)) * np.float32(math.log2(math.e))))
+    codes, scales, _ = oracle.quantize_qk4(bits, prescale=c2)
+    xv = oracle.bf16_to_f64(bits).astype(np.float32) * np.float32(c2)  # binary32 products
+    for s_ in range(S):
+        for blk in range(D // 32):
+            v = xv[0, 0, s_, blk * 32:(blk + 1) * 32].astype(np.float64)
+            e = _block_scale_numpy(v, 2)
+            assert scales[0, 0, s_, blk] == e + 127
+            for i in range(32):
+                a = v[i] * 2.0**-e
+                want = (8 if math.copysign(1.0, a) < 0 else 0) | _nearest_even_bruteforce(abs(a), table)
+                byte = codes[0, 0, s_, (blk * 32 + i) // 2]
+                got = (byte >> 4) if i % 2 else (byte & 15)
+                assert got == want, (s_, blk, i, a)
+    c1, s1, _ = oracle.quantize_qk4(bits)
+    c8, s8, _ = oracle.quantize_qk4(bits, prescale=8.0)
+    assert np.array_equal(c1, c8) and np.array_equal(s8.astype(int), s1.astype(int) + 3)
+
+
 def test_mxfp4_bits_per_element_and_nonfinite():
     g = gold("mx_bits_per_element.json")
     D = 128
