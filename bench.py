@@ -131,11 +131,12 @@ def main():
         O = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
         stream = torch.cuda.current_stream()
+        c2 = qfa.qfa_exp2_scale(w.scale)  # Q carries softmax_scale * log2 e
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
 
         def step(i=None):
-            qfa.qfa_quantize_qk4(q, B, Hq, S, D, 32, 0, q4, q4s, None, stream)
-            qfa.qfa_quantize_qk4(k, B, Hkv, S, D, 32, int(w.smooth), k4, k4s, kbar, stream)
+            qfa.qfa_quantize_qk4(q, B, Hq, S, D, 32, 0, c2, q4, q4s, None, stream)
+            qfa.qfa_quantize_qk4(k, B, Hkv, S, D, 32, int(w.smooth), 1.0, k4, k4s, kbar, stream)
             qfa.qfa_quantize_v8(v, B, Hkv, S, D, 32, v8, v8s, stream)
             if i is not None:
                 ev[i][0].record(stream)
@@ -190,6 +191,7 @@ def main():
         k4d, k4sd, _ = qfa.quantize_qk4(di["k"])
         v8d, v8sd = qfa.quantize_v8(di["v"])
         qd = di["q"]
+        c2d = qfa.qfa_exp2_scale(wd.scale)
         del di
         q4d = torch.empty((Bd, Hqd, 1, Dd // 2), dtype=torch.uint8, device=dev)
         q4sd = torch.empty((Bd, Hqd, 1, Dd // 32), dtype=torch.uint8, device=dev)
@@ -202,7 +204,7 @@ def main():
                   for _ in range(args.steps)]
 
         def dstep(i=None):
-            qfa.qfa_quantize_qk4(qd, Bd, Hqd, 1, Dd, 32, 0, q4d, q4sd, None, stream)
+            qfa.qfa_quantize_qk4(qd, Bd, Hqd, 1, Dd, 32, 0, c2d, q4d, q4sd, None, stream)
             if i is not None:
                 dev_ev[i][0].record(stream)
             qfa.qfa_fwd_decode(q4d, q4sd, k4d, k4sd, None, None, v8d, v8sd, Bd, Hqd, Hkvd, L, None, Dd, wd.scale,

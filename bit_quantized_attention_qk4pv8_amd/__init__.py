@@ -28,7 +28,8 @@ QFA_ERR_HIP = 4
 
 EXPORTS = (
     "qfa_quantize_qk4", "qfa_quantize_v8", "qfa_fwd_prefill", "qfa_fwd_decode",
-    "qfa_decode_workspace_bytes", "qfa_decode_default_splits", "qfa_status_string", "qfa_version",
+    "qfa_decode_workspace_bytes", "qfa_decode_default_splits", "qfa_exp2_scale", "qfa_status_string",
+    "qfa_version",
 )
 
 _lib = None
@@ -49,7 +50,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.qfa_quantize_qk4.restype = I
-        L.qfa_quantize_qk4.argtypes = [P, I, I, I, I, I, I, P, P, P, P]
+        L.qfa_quantize_qk4.argtypes = [P, I, I, I, I, I, I, F, P, P, P, P]
         L.qfa_quantize_v8.restype = I
         L.qfa_quantize_v8.argtypes = [P, I, I, I, I, I, P, P, P]
         L.qfa_fwd_prefill.restype = I
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.qfa_decode_workspace_bytes.argtypes = [I, I, I, I]
         L.qfa_decode_default_splits.restype = I
         L.qfa_decode_default_splits.argtypes = [I, I, I]
+        L.qfa_exp2_scale.restype = F
+        L.qfa_exp2_scale.argtypes = [F]
         L.qfa_status_string.restype = ctypes.c_char_p
         L.qfa_status_string.argtypes = [I]
         L.qfa_version.restype = I
@@ -109,9 +112,14 @@ def qfa_decode_default_splits(B: int, Hkv: int, S_kv_max: int) -> int:
     return lib().qfa_decode_default_splits(B, Hkv, S_kv_max)
 
 
-def qfa_quantize_qk4(x, B, H, S, D, block_size, smooth, codes, scales, kbar, stream=None):
+def qfa_exp2_scale(softmax_scale: float) -> float:
+    return lib().qfa_exp2_scale(float(softmax_scale))
+
+
+def qfa_quantize_qk4(x, B, H, S, D, block_size, smooth, prescale, codes, scales, kbar, stream=None):
     _check("qfa_quantize_qk4", lib().qfa_quantize_qk4(_ptr(_u16(x)), B, H, S, D, block_size, int(smooth),
-                                                      _ptr(codes), _ptr(scales), _ptr(kbar), _stream(stream)))
+                                                      float(prescale), _ptr(codes), _ptr(scales), _ptr(kbar),
+                                                      _stream(stream)))
 
 
 def qfa_quantize_v8(v, B, H, S, D, block_size, codes, scales, stream=None):
@@ -139,13 +147,15 @@ def qfa_fwd_decode(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max
 
 
 # ----------------------------------------------------------------------------- allocating helpers
-def quantize_qk4(x: torch.Tensor, smooth: bool = False, stream=None):
-    """x bf16 [B,H,S,D] on the GPU -> (codes u8 [B,H,S,D/2], scales u8 [B,H,S,D/32], kbar bf16 or None)."""
+def quantize_qk4(x: torch.Tensor, smooth: bool = False, prescale: float = 1.0, stream=None):
+    """x bf16 [B,H,S,D] on the GPU -> (codes u8 [B,H,S,D/2], scales u8 [B,H,S,D/32], kbar bf16 or None).
+
+    Q takes prescale = qfa_exp2_scale(softmax_scale), K takes 1."""
     B, H, S, D = x.shape
     codes = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((B, H, S, D // 32), dtype=torch.uint8, device=x.device)
     kbar = torch.empty((B, H, (S + 127) // 128, D), dtype=torch.bfloat16, device=x.device) if smooth else None
-    qfa_quantize_qk4(x, B, H, S, D, 32, smooth, codes, scales, kbar, stream)
+    qfa_quantize_qk4(x, B, H, S, D, 32, smooth, prescale, codes, scales, kbar, stream)
     return codes, scales, kbar
 
 

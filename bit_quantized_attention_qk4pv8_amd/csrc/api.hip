@@ -45,16 +45,19 @@ const char* qfa_status_string(qfa_status status) {
 
 int qfa_version(void) { return kVersion; }
 
+float qfa_exp2_scale(float softmax_scale) { return softmax_scale * kLog2e; }
+
 qfa_status qfa_quantize_qk4(const uint16_t* x, int B, int H, int S, int D, int block_size, int smooth,
-                            uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t stream) {
+                            float prescale, uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t stream) {
   if (block_size != 32 || !qk_dim_ok(D)) return QFA_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || S < 0 || (long long)B * H > 65535) return QFA_ERR_INVALID_ARG;
   if (smooth != 0 && smooth != 1) return QFA_ERR_INVALID_ARG;
+  if (!(prescale > 0.0f) || !isfinite(prescale)) return QFA_ERR_INVALID_ARG;
   if ((smooth == 1) != (kbar != nullptr)) return QFA_ERR_INVALID_ARG;
   if ((long long)B * H * S == 0) return QFA_OK;
   if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return QFA_ERR_INVALID_ARG;
   if (kbar && !aligned16(kbar)) return QFA_ERR_INVALID_ARG;
-  return from_hip(qfa::launch_quant_qk4(x, B, H, S, D, smooth, codes, scales, kbar, stream));
+  return from_hip(qfa::launch_quant_qk4(x, B, H, S, D, smooth, prescale, codes, scales, kbar, stream));
 }
 
 qfa_status qfa_quantize_v8(const uint16_t* v, int B, int H, int S, int D, int block_size, uint8_t* codes,

@@ -63,19 +63,19 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
       ld.issue_k(t + 1, bufs + ((t + 1) & 1) * TL::STRIDE, 0);
       ld.issue_v(t + 1, bufs + ((t + 1) & 1) * TL::STRIDE + TL::V_OFF, 0);
     }
-    float delta = 0.0f;
+    float d32 = 0.0f;
     if (COMP) {
       if (t == t0 || (t & 31) == 0)
         compute_delta<D>(dl, a.kbar + (size_t)bg * ntk_max * D, ntk, t & ~31,
                          a.qbf + ((size_t)b * a.Hq + gk * a.G + 32 * rc) * D, D, a.G - 32 * rc);
-      delta = dl[(t & 31) * 32 + n];
+      d32 = a.c2 * dl[(t & 31) * 32 + n];
     }
     uint8_t* buf = bufs + (t & 1) * TL::STRIDE;
     v16f s[4];
     v8i pb[2];
     int pscale;
     qk_tile<D>(st, lo, buf, s);
-    softmax_tile<D>(st, s, t, kTile * t + kTile > L, L - 1, a.c2, delta, pb, pscale);
+    softmax_tile<D, COMP>(st, s, t, kTile * t + kTile > L, L - 1, d32, pb, pscale);
     pv_tile<D>(st, lo, buf + TL::V_OFF, pb, pscale);
     wait_vmem_all();
     if (t + 1 < t1) ld.fixup(t + 1, bufs + ((t + 1) & 1) * TL::STRIDE);

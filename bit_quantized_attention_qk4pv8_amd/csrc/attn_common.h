@@ -213,15 +213,17 @@ struct RowState {
   v8i ones;        // FP8 1.0 in every byte: the A operand of the denominator product
 };
 
-// Softmax step of one tile: masks keys > jlim (when need_mask), moves the
-// running max m on the integer grid (log2 units), and converts
-// P = E4M3(256 * 2^(s*c2 + c2*delta - m)) into pb, the B operand of the P V
-// product (pb[h] covers keys 64h .. 64h+63).  pscale receives the E8M0 code of
-// 2^(m - m_ref) that the P V product applies.  O and l are touched only by the
-// rare frame rebase.
-template <int D>
-__device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int t, bool need_mask, int jlim, float c2,
-                                             float delta, v8i (&pb)[2], int& pscale) {
+// Softmax step of one tile.  s holds S' = Q'K^T, the logits in log2 units
+// (Q carries the factor softmax_scale * log2 e).  Masks keys > jlim (when
+// need_mask), adds the compensation offset d32 = fl32(c2 * delta) (COMP),
+// moves the running max m on the integer grid and converts
+// P = E4M3(256 * 2^(y - m)) into pb, the B operand of the P V product (pb[h]
+// covers keys 64h .. 64h+63).  pscale receives the E8M0 code of 2^(m - m_ref)
+// that the P V product applies.  O and l are touched only by the rare frame
+// rebase.
+template <int D, bool COMP>
+__device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int t, bool need_mask, int jlim,
+                                             float d32, v8i (&pb)[2], int& pscale) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   // ---- mask (diagonal / ragged tiles only); score s[c][rr] is key 128t + 32c + 16g + rr.
@@ -239,6 +241,12 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
         s[c][rr] = __int_as_float((__float_as_int(s[c][rr]) & ~msk) | (int)(0xFF800000u & (uint32_t)msk));
       }
     }
+  }
+  if (COMP) {  // y = fl32(S' + d32)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) s[c][rr] += d32;
   }
 
   // ---- row max (two left-associated chains: max(max(m, a), b) compiles to
@@ -263,10 +271,7 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
   }
   // Running max on the integer grid: every rescale factor is an exact power of
   // two, applied through the E8M0 scale of the P operand (no VALU work on O).
-  const float dlt = c2 * delta;
-  const float mt = __builtin_ceilf(__builtin_fmaf(mx, c2, dlt));
-  const float mn = __builtin_fmaxf(st.m, mt);
-  const float beta = (mn == -__builtin_inff()) ? 0.0f : dlt - mn;
+  const float mn = __builtin_fmaxf(st.m, __builtin_ceilf(mx));
   if (st.m_ref == -__builtin_inff()) st.m_ref = mn;  // first visible key fixes the frame
   st.m = mn;
   // Keep 2^(m - m_ref) inside the E8M0 range: rebase the frame when it grows
@@ -283,21 +288,35 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
   }
   pscale = (mn == -__builtin_inff()) ? kScaleOne : kScaleOne + (int)(mn - st.m_ref);
 
-  // ---- P8 = E4M3(256 * 2^(s*c2 + beta)), packed as the B operand of O^T += V^T P^T
+  // ---- P8 = E4M3(256 * 2^(y - m)), packed as the B operand of O^T += V^T P^T.
+  // The conversion divides by its scale operand, so 2^(m - 8) there turns
+  // 2^y into 256 * 2^(y - m) exactly, with no per-score subtraction.  That
+  // needs 2^y and the scale in binary32 range: while |m| <= 64 the keys that
+  // can give a non-zero code (y > m - 18) have 2^y in [2^-82, 2^64].  A wave
+  // with a row outside subtracts m from every score first.
+  const float e = (mn == -__builtin_inff()) ? 0.0f : mn;
+  const bool far = __builtin_amdgcn_ballot_w64(__builtin_fabsf(e) > 64.0f) != 0;
+  if (far) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) s[c][rr] -= e;
+  }
+  const float cs = far ? 0x1p-8f : __builtin_ldexpf(1.0f, (int)e - 8);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int c = 2 * h + (k >> 2);
       const int r0 = 4 * (k & 3);
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r0 + 0], c2, beta));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r0 + 1], c2, beta));
-      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r0 + 2], c2, beta));
-      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r0 + 3], c2, beta));
+      const float p0 = __builtin_amdgcn_exp2f(s[c][r0 + 0]);
+      const float p1 = __builtin_amdgcn_exp2f(s[c][r0 + 1]);
+      const float p2 = __builtin_amdgcn_exp2f(s[c][r0 + 2]);
+      const float p3 = __builtin_amdgcn_exp2f(s[c][r0 + 3]);
       // the old value of the destination is dead (both halves are written): reuse p0's register
       v2s w = __builtin_bit_cast(v2s, p0);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p0, p1, 0x1p-8f, false);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p2, p3, 0x1p-8f, true);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p0, p1, cs, false);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p2, p3, cs, true);
       pb[h][k] = __builtin_bit_cast(int, w);
     }
 }

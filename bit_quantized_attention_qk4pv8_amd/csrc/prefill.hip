@@ -144,9 +144,9 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
     phase_barrier();
     // ---- softmax phase of tile t; A waves then wait for the DMA issued above
     if (t < Tw) {
-      const float delta = COMP ? dl[(t & 31) * 32 + n] : 0.0f;
+      const float d32 = COMP ? a.c2 * dl[(t & 31) * 32 + n] : 0.0f;
       const bool need_mask = (kTile * t + kTile - 1 > jmin_w) || (kTile * t + kTile > L);
-      softmax_tile<D>(st, s, t, need_mask, jlim, a.c2, delta, pb, pscale);
+      softmax_tile<D, COMP>(st, s, t, need_mask, jlim, d32, pb, pscale);
     }
     if (half == 0) {
       wait_vmem_all();

@@ -65,8 +65,8 @@ __device__ __forceinline__ v16f mfma_fp8_32x32x64(v8i a, v8i b, v16f c, int sa, 
 }
 
 // ---------------------------------------------------------------- launchers (host side)
-hipError_t launch_quant_qk4(const uint16_t* x, int B, int H, int S, int D, int smooth, uint8_t* codes,
-                            uint8_t* scales, uint16_t* kbar, hipStream_t s);
+hipError_t launch_quant_qk4(const uint16_t* x, int B, int H, int S, int D, int smooth, float prescale,
+                            uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t s);
 hipError_t launch_quant_v8(const uint16_t* v, int B, int H, int S, int D, uint8_t* codes, uint8_t* scales,
                            hipStream_t s);
 

@@ -6,6 +6,8 @@
 //    Q and K to 4 bits with block scales; block recipe per the hnwysp.cn
 //    MXAttention/MXFP4 notes, sections 2.3 and 5.2: amax -> power-of-two scale ->
 //    divide -> round to nearest even).
+//  * Q is multiplied by c2 = fl32(softmax_scale * log2 e) in binary32 first
+//    (prescale), so that Q'K^T is the softmax exponent in log2 units.
 //  * K smoothing for the rank-one compensation: per 128-token block channel
 //    means, summed exactly in binary64, divided by the number of present tokens
 //    and rounded to bf16; the quantised tensor is fl32(K - Kbar).
@@ -39,8 +41,8 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
 
 template <int D>
 __global__ void __launch_bounds__(256) k_quant_qk4(const uint16_t* __restrict__ x, int S, int ntiles, int smooth,
-                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                   uint16_t* __restrict__ kbar) {
+                                                   float prescale, uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales, uint16_t* __restrict__ kbar) {
   constexpr int NB = D / kBlock;
   __shared__ float kb[D];
   const int tile = blockIdx.x;
@@ -75,6 +77,10 @@ __global__ void __launch_bounds__(256) k_quant_qk4(const uint16_t* __restrict__ 
     if (smooth) {
 #pragma unroll
       for (int i = 0; i < kBlock; ++i) v[i] = v[i] - kb[blk * kBlock + i];
+    }
+    if (prescale != 1.0f) {  // Q: fl32(q * c2)
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) v[i] = v[i] * prescale;
     }
     uint32_t amax = 0u, nonfinite = 0u;
 #pragma unroll
@@ -151,13 +157,13 @@ __global__ void __launch_bounds__(D) k_quant_v8(const uint16_t* __restrict__ v, 
   scales[(bh * nblk + blk) * D + c] = sc;
 }
 
-hipError_t launch_quant_qk4(const uint16_t* x, int B, int H, int S, int D, int smooth, uint8_t* codes,
-                            uint8_t* scales, uint16_t* kbar, hipStream_t s) {
+hipError_t launch_quant_qk4(const uint16_t* x, int B, int H, int S, int D, int smooth, float prescale,
+                            uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t s) {
   const int ntiles = (S + kTile - 1) / kTile;
   dim3 grid(ntiles, B * H);
   switch (D) {
 #define QFA_QK4_CASE(DD) \
-  case DD: hipLaunchKernelGGL(k_quant_qk4<DD>, grid, dim3(256), 0, s, x, S, ntiles, smooth, codes, scales, kbar); break;
+  case DD: hipLaunchKernelGGL(k_quant_qk4<DD>, grid, dim3(256), 0, s, x, S, ntiles, smooth, prescale, codes, scales, kbar); break;
     QFA_QK4_CASE(32) QFA_QK4_CASE(64) QFA_QK4_CASE(96) QFA_QK4_CASE(128) QFA_QK4_CASE(160) QFA_QK4_CASE(192)
     QFA_QK4_CASE(224) QFA_QK4_CASE(256)
 #undef QFA_QK4_CASE

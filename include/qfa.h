@@ -67,17 +67,28 @@ typedef enum qfa_status {
 } qfa_status;
 
 /*
+ * The factor Q is multiplied by before it is quantised:
+ * c2 = fl32(softmax_scale * fl32(log2 e)).  S = Q K^T / sqrt(d) is
+ * exponentiated in base 2, and with c2 applied to Q the product Q'K^T is the
+ * exponent argument in log2 units (the pages do not say where the scale
+ * enters).  Host arithmetic only.
+ */
+float qfa_exp2_scale(float softmax_scale);
+
+/*
  * Online Q or K quantisation to MXFP4 (MpFA abstract: "online quantization";
  * block quantiser of the MXFP4 notes, sections 2.3 and 5.2).
- *   x       bf16 [B][H][S][D]
- *   smooth  0: quantise x.  1 (K only): also write kbar and quantise the
- *           smoothed tensor fl32(x - Kbar_block) -- the K side of the rank-one
- *           smoothing compensation.  kbar must be NULL iff smooth == 0.
- *   codes   out [B][H][S][D/2], scales out [B][H][S][D/32], kbar out as above.
+ *   x         bf16 [B][H][S][D]
+ *   smooth    0: quantise x.  1 (K only): also write kbar and quantise the
+ *             smoothed tensor fl32(x - Kbar_block) -- the K side of the rank-one
+ *             smoothing compensation.  kbar must be NULL iff smooth == 0.
+ *   prescale  each element is multiplied by it in binary32 before quantisation:
+ *             qfa_exp2_scale(softmax_scale) for Q, 1 for K.  Must be finite and > 0.
+ *   codes     out [B][H][S][D/2], scales out [B][H][S][D/32], kbar out as above.
  * Deterministic: codes, scales and kbar are bit-exact functions of x.
  */
 qfa_status qfa_quantize_qk4(const uint16_t* x, int B, int H, int S, int D, int block_size, int smooth,
-                            uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t stream);
+                            float prescale, uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t stream);
 
 /*
  * V quantisation to FP8 E4M3 with one E8M0 scale per (32 consecutive tokens,
@@ -90,20 +101,22 @@ qfa_status qfa_quantize_v8(const uint16_t* v, int B, int H, int S, int D, int bl
 
 /*
  * Prefill forward (MpFA abstract; online softmax per the FP4 tutorial's
- * section "注意力慢在哪儿").  For each query row i of head h (kv head
- * h / (Hq/Hkv)) the 128-token key tiles are visited in ascending order:
- *   s_j = scale * (q4 . k4_j + delta_{i,tile})   (delta = q_bf16 . Kbar_tile,
- *                                                  only when kbar != NULL)
- *   m'  = max(m, ceil(max_j log2e * s_j))   (log2 units, an integer bound
- *                                             on the row max)
- *   P8_j = E4M3(256 * 2^(log2e * s_j - m'))
- *   l   = 2^(m - m') l + sum_j P8_j;  O = 2^(m - m') O + sum_j P8_j V8_j
+ * section "注意力慢在哪儿").  Q must be quantised with prescale
+ * qfa_exp2_scale(softmax_scale), so s_j = q4 . k4_j is the logit of key j in
+ * log2 units.  For each query row i of head h (kv head h / (Hq/Hkv)) the
+ * 128-token key tiles are visited in ascending order:
+ *   y_j  = fl32(s_j + fl32(c2 * delta))   (delta = q_bf16 . Kbar_tile, only
+ *                                          when kbar != NULL)
+ *   m'   = max(m, ceil(max_j y_j))        (an integer bound on the row max)
+ *   P8_j = E4M3(256 * 2^(y_j - m'))
+ *   l    = 2^(m - m') l + sum_j P8_j;  O = 2^(m - m') O + sum_j P8_j V8_j
  * and O / l, LSE = ln(l / 256) + m ln 2 are written.  Because m is an integer
- * the rescale factors are exact powers of two and the P codes do not depend
- * on how the key range is cut into tiles or splits.  delta is the exactly
- * rounded binary32 value of the bf16 dot product.  S and P never reach
- * memory.  Causal masks are bottom-right aligned: key j is visible to query i
- * iff j <= i + (S_kv - S_q); a row with no visible key gets O = 0, LSE = -inf.
+ * the rescale factors are exact powers of two, and E4M3 rounding commutes
+ * with them, so without the compensation the P codes do not depend on how
+ * the key range is cut into tiles or splits.  delta is the exactly rounded
+ * binary32 value of the bf16 dot product.  S and P never reach memory.
+ * Causal masks are bottom-right aligned: key j is visible to query i iff
+ * j <= i + (S_kv - S_q); a row with no visible key gets O = 0, LSE = -inf.
  *   q4, q4s      MXFP4 Q [B][Hq][S_q][D/2], [B][Hq][S_q][D/32]
  *   k4, k4s      MXFP4 K [B][Hkv][S_kv][D/2], [..][D/32] (smoothed if kbar)
  *   kbar, q_bf16 both NULL (no compensation) or both set:
@@ -125,7 +138,8 @@ qfa_status qfa_fwd_prefill(const uint8_t* q4, const uint8_t* q4s, const uint8_t*
  * yields a normalised partial (O_s, LSE_s) in `workspace`, and a second kernel
  * merges them: LSE = log sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s.  Runs
  * with no key get weight 0.  No causal mask.
- *   q4, q4s        MXFP4 Q [B][Hq][1][D/2], [B][Hq][1][D/32]
+ *   q4, q4s        MXFP4 Q [B][Hq][1][D/2], [B][Hq][1][D/32], quantised with
+ *                  prescale qfa_exp2_scale(softmax_scale) as for prefill
  *   k4, k4s, v8, v8s   the pre-quantised KV cache, S_kv_max tokens per sequence
  *   kbar, q_bf16   both NULL or both set, as for prefill
  *   num_splits     in/out: 0 lets the library choose (written back); > 0 is used

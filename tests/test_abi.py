@@ -6,6 +6,7 @@ rejects the call on the host.
 """
 import ctypes
 import json
+import math
 import os
 import re
 
@@ -53,6 +54,13 @@ def test_workspace_bytes_and_default_splits():
     assert qfa.qfa_decode_default_splits(1, 1, 0) == 1
 
 
+def test_exp2_scale_is_the_binary32_product():
+    import numpy as np
+    for sc in (0.125, 1 / math.sqrt(128), 1 / math.sqrt(64), 1.0, 3e-3, 7.5):
+        want = np.float32(sc) * np.float32(math.log2(math.e))   # both operands and the product in binary32
+        assert np.float32(qfa.qfa_exp2_scale(sc)) == want
+
+
 def _call_raw(fn, *args):
     return getattr(qfa.lib(), fn)(*args)
 
@@ -62,11 +70,15 @@ def test_validation_rejects_before_launch():
     fake = P(4096)          # 16-byte aligned, never dereferenced: validation fails first
     odd = P(4097)
     # block size and head dimension
-    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 64, 16, 0, fake, fake, None, None) == qfa.QFA_ERR_UNSUPPORTED
-    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 48, 32, 0, fake, fake, None, None) == qfa.QFA_ERR_UNSUPPORTED
+    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 64, 16, 0, 1.0, fake, fake, None, None) == qfa.QFA_ERR_UNSUPPORTED
+    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 48, 32, 0, 1.0, fake, fake, None, None) == qfa.QFA_ERR_UNSUPPORTED
     # kbar must be given iff smooth
-    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 64, 32, 1, fake, fake, None, None) == qfa.QFA_ERR_INVALID_ARG
-    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 64, 32, 0, fake, fake, fake, None) == qfa.QFA_ERR_INVALID_ARG
+    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 64, 32, 1, 1.0, fake, fake, None, None) == qfa.QFA_ERR_INVALID_ARG
+    assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 64, 32, 0, 1.0, fake, fake, fake, None) == qfa.QFA_ERR_INVALID_ARG
+    # the Q prescale must be a finite positive number
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert _call_raw("qfa_quantize_qk4", fake, 1, 1, 1, 64, 32, 0, bad, fake, fake, None, None) == \
+            qfa.QFA_ERR_INVALID_ARG
     # misaligned input
     assert _call_raw("qfa_quantize_v8", odd, 1, 1, 1, 64, 32, fake, fake, None) == qfa.QFA_ERR_INVALID_ARG
     # empty problem: nothing to do

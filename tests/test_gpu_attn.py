@@ -35,7 +35,7 @@ def _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed, k_offset=0.0, q_scale=1.0):
 def _gpu_prefill(q, k, v, causal, scale, smooth):
     B, Hq, Sq, D = q.shape
     Skv = k.shape[2]
-    q4, q4s, _ = qfa.quantize_qk4(q)
+    q4, q4s, _ = qfa.quantize_qk4(q, prescale=qfa.qfa_exp2_scale(scale))
     k4, k4s, kbar = qfa.quantize_qk4(k, smooth=smooth)
     v8, v8s = qfa.quantize_v8(v)
     O, lse = qfa.fwd_prefill(q4, q4s, k4, k4s, v8, v8s, Skv, causal, scale, kbar=kbar,
@@ -116,7 +116,7 @@ def test_prefill_workload_sampled(name, nrows):
 def _gpu_decode(q, k, v, num_splits, kv_lens=None, smooth=False):
     B, Hq, _, D = q.shape
     Smax = k.shape[2]
-    q4, q4s, _ = qfa.quantize_qk4(q)
+    q4, q4s, _ = qfa.quantize_qk4(q, prescale=qfa.qfa_exp2_scale(1 / math.sqrt(D)))
     k4, k4s, kbar = qfa.quantize_qk4(k, smooth=smooth)
     v8, v8s = qfa.quantize_v8(v)
     lens = None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32, device="cuda")
@@ -159,7 +159,8 @@ def _decode_oracle_smooth(q, k, v, rows, splits, kv_lens):
         per = max(1, -(-nt // splits))
         kc, ks, kbar = oracle.quantize_qk4(np.ascontiguousarray(kb[b:b + 1, g:g + 1, :L]), smooth=True)
         vc, vs = oracle.quantize_v8(np.ascontiguousarray(vb[b:b + 1, g:g + 1, :L]))
-        qc, qs, _ = oracle.quantize_qk4(np.ascontiguousarray(qb[b:b + 1, h:h + 1]))
+        qc, qs, _ = oracle.quantize_qk4(np.ascontiguousarray(qb[b:b + 1, h:h + 1]),
+                                        prescale=oracle.exp2_scale(1 / math.sqrt(D)))
         O, l = oracle.attn_quant_rows(oracle.dequant_qk4(qc, qs)[0, 0], np.zeros(1, np.int64),
                                       oracle.dequant_qk4(kc, ks)[0, 0], oracle.dequant_v8(vc[0, 0], vs[0, 0], L),
                                       1, False, 1 / math.sqrt(D), Qc=oracle.bf16_to_f64(qb[b, h]),

@@ -11,11 +11,11 @@ from gpu_util import say, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _check_qk4(x: torch.Tensor, smooth: bool, label: str):
-    say("quantize_qk4", label, tuple(x.shape), "smooth", smooth)
-    codes, scales, kbar = qfa.quantize_qk4(x, smooth=smooth)
+def _check_qk4(x: torch.Tensor, smooth: bool, label: str, prescale: float = 1.0):
+    say("quantize_qk4", label, tuple(x.shape), "smooth", smooth, "prescale", prescale)
+    codes, scales, kbar = qfa.quantize_qk4(x, smooth=smooth, prescale=prescale)
     torch.cuda.synchronize()
-    oc, os_, ok = oracle.quantize_qk4(bf16_bits(x), smooth=smooth)
+    oc, os_, ok = oracle.quantize_qk4(bf16_bits(x), smooth=smooth, prescale=prescale)
     assert np.array_equal(to_np(codes), oc), label + ": codes differ"
     assert np.array_equal(to_np(scales), os_), label + ": scales differ"
     if smooth:
@@ -41,6 +41,8 @@ def test_qk4_bitexact_shapes(shape, smooth):
     x[..., 0, :] = 0.0                                            # all-zero row
     x += torch.randn((1, shape[1], 1, shape[3]), generator=g, device="cuda") * 3.0 * smooth
     _check_qk4(x.to(torch.bfloat16), smooth, "shape%s" % (shape,))
+    # Q side: the softmax factor applied in binary32 before the block scale is chosen
+    _check_qk4(x.to(torch.bfloat16), False, "shape%s.prescaled" % (shape,), prescale=oracle.exp2_scale(0.0883883))
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 75, 64), (2, 3, 1000, 128), (1, 1, 31, 128), (1, 1, 64, 256)])
@@ -60,6 +62,7 @@ def test_quantizers_nonfinite_and_tiny():
     x[0, 0, 4, 32:64] = -0.0
     xb = x.to(torch.bfloat16)
     _check_qk4(xb, False, "nonfinite")
+    _check_qk4(xb, False, "nonfinite.prescaled", prescale=oracle.exp2_scale(0.125))
     _check_v8(xb, "nonfinite")
 
 
@@ -67,7 +70,7 @@ def test_quantizers_nonfinite_and_tiny():
 def test_workload_tensors_bitexact(name):
     w = WORKLOADS[name]
     inp = make_inputs(w, seed=0)
-    _check_qk4(inp["q"], False, name + ".q")
+    _check_qk4(inp["q"], False, name + ".q", prescale=oracle.exp2_scale(w.scale))
     _check_qk4(inp["k"], w.smooth, name + ".k")
     _check_v8(inp["v"], name + ".v")
 
@@ -77,7 +80,7 @@ def test_long128k_and_decode_slices_bitexact():
     inp = make_inputs(w, seed=0)
     _check_qk4(inp["k"][:, :2].contiguous(), False, "long128k.k[:2]")
     _check_v8(inp["v"][:, 6:].contiguous(), "long128k.v[6:]")
-    _check_qk4(inp["q"][:, 5:7].contiguous(), False, "long128k.q[5:7]")
+    _check_qk4(inp["q"][:, 5:7].contiguous(), False, "long128k.q[5:7]", prescale=oracle.exp2_scale(w.scale))
     del inp
     wd = WORKLOADS["decode"]
     inp = make_inputs(wd, seed=0, B_override=3)
