@@ -157,6 +157,50 @@ struct TileLoader {
     }
   }
 
+  // Fixed-shape issue of the code instructions: each of the NW waves makes
+  // the same SLOTS instructions per (K, V) tile pair, so they can sit between
+  // MFMAs without a branch.  Slot k (a compile-time value after unrolling):
+  //   k <  KCS   K codes, instruction wave + NW * k
+  //   k >= KCS   V codes, instruction wave + NW * (k - KCS)
+  // An instruction past the end of its region, or of a tile that is not
+  // wanted (ek / ev false), reads nothing (range 0) and writes its zeros to
+  // `trash`, 1 KB of LDS that nothing reads.  The scale instructions are
+  // issued by issue_scales.
+  static constexpr int KCS = (TL::NK + NW - 1) / NW;
+  static constexpr int VCS = (TL::NV + NW - 1) / NW;
+  static constexpr int SLOTS = KCS + VCS;
+  __device__ __forceinline__ void dma_slot(int k, int tk, uint8_t* kreg, bool ek, int tv, uint8_t* vreg, bool ev,
+                                           int wave, uint8_t* trash) const {
+    if (k < KCS) {
+      const int ins = wave + NW * k;
+      const bool e = ek && ins < TL::NK;
+      const __amdgpu_buffer_rsrc_t r = rsrc_at(kc, e ? kc_bytes : 0u, (uint32_t)tk * TL::KC + (e ? ins : 0) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(e ? kreg + ins * 1024 : trash), 16, vkw, 0, 0, 0);
+    } else if (k < SLOTS) {
+      const int ins = wave + NW * (k - KCS);
+      const bool e = ev && ins < TL::NV;
+      const __amdgpu_buffer_rsrc_t r = rsrc_at(vc, e ? vc_bytes : 0u, (uint32_t)tv * TL::VC + (e ? ins : 0) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(e ? vreg + ins * 1024 : trash), 16, vv, 0, 0, 0);
+    }
+  }
+  // Scale instructions of a tile pair: wave i < NKS loads K-scale dword block
+  // i, wave NKS the V scales; returns how many loads this wave issued.
+  __device__ __forceinline__ int issue_scales(int tk, uint8_t* kreg, bool ek, int tv, uint8_t* vreg, bool ev,
+                                              int wave) const {
+    const int lane = threadIdx.x & 63;
+    if (ek && wave < TL::NKS) {
+      const __amdgpu_buffer_rsrc_t r = rsrc_at(ks, ks_bytes, (uint32_t)tk * TL::KS_BYTES + wave * 256);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(kreg + TL::KC + wave * 256), 4, lane * 4, 0, 0, 0);
+      return 1;
+    }
+    if (ev && wave == TL::NKS) {
+      const __amdgpu_buffer_rsrc_t r = rsrc_at(vs, vs_bytes, (uint32_t)tv * TL::VS_BYTES);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(vreg + TL::VC), 16, lane * 16, 0, 0, 0);
+      return 1;
+    }
+    return 0;
+  }
+
   // D = 64 with an odd key count: the last token's two scale bytes share a
   // dword with bytes past the end, which the range check zeroes; patch them
   // after the DMA has landed (called between the wait and the barrier).
@@ -367,9 +411,17 @@ __device__ __forceinline__ void load_v_op(const uint8_t* vreg, const LaneOffs<D>
 // ahead and the first two K blocks during the last P V products, so the MFMAs
 // issue back to back while LDS reads stay in flight.  The scheduler fences
 // keep this order within the register budget of two waves per SIMD.
-template <int D>
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// hook(k) runs after the k-th MFMA step (k = 0 .. 2 D/32 + 3), inside the
+// scheduling fences: a place for instructions that should issue while the
+// matrix unit is busy.
+template <int D, class Hook = NoHook>
 __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D>& lo, const uint8_t* vreg,
-                                           const v8i (&pb)[2], int pscale, const uint8_t* kreg, v16f (&s)[4]) {
+                                           const v8i (&pb)[2], int pscale, const uint8_t* kreg, v16f (&s)[4],
+                                           const Hook& hook = Hook()) {
   constexpr int NQ = 2 * (D / 32);  // P V products (excluding the denominator)
   constexpr int R = 3;              // V operands in flight
   v8i va[R];
@@ -387,12 +439,14 @@ __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D>& l
       load_v_op<D>(vreg, lo, q + R, va[q % R], vs[q % R]);
     else if (q + R - NQ < 2)
       load_k_blk<D>(kreg, lo, q + R - NQ, kb[q + R - NQ]);
+    hook(q);
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     __builtin_amdgcn_sched_barrier(0);
     qk_blk<D>(st, kb[c & 1], s[c]);
     if (c + 2 < 4) load_k_blk<D>(kreg, lo, c + 2, kb[c & 1]);
+    hook(NQ + c);
   }
   __builtin_amdgcn_sched_barrier(0);
 }

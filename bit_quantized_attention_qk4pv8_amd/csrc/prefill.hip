@@ -10,44 +10,90 @@
 // Schedule.  On gfx950 a wave's MFMA and VALU instructions do not overlap each
 // other, but an MFMA of one wave runs alongside VALU work of another wave on
 // the same SIMD.  The softmax of a tile is pure VALU (exp, FP8 conversion,
-// max) and the two products are pure MFMA, so each SIMD hosts two waves whose
-// phases are kept opposite by workgroup barriers:
+// max) and the two products are pure MFMA, so each SIMD hosts two waves that
+// run the same loop -- products of tile t (P V(t-1), S(t) = K(t) Q^T), then
+// the softmax of tile t -- half an iteration apart.  One workgroup barrier per
+// iteration keeps them there: wave A (rows 0..31 of a unit) arrives after its
+// softmax, wave B (rows 32..63) after its products, so between two barriers
 //
-//   phase   wave A (rows 0..31 of a unit)     wave B (rows 32..63 of the unit)
-//   2t      P V(t-1), S(t) = K(t) Q^T          softmax(t-1)
-//   2t+1    softmax(t)                         P V(t-1), S(t)
+//   wave A:  products(t+1)   softmax(t+1)
+//   wave B:  softmax(t)      products(t+1)
+//
+// and each side may run ahead into its second half while the other finishes
+// its first.  The products run at raised issue priority, so an MFMA issues as
+// soon as the matrix unit is free and the VALU work of the other wave fills
+// the gaps.
 //
 // A workgroup is 8 waves: waves w and w+4 share SIMD w % 4 and own one unit
 // (query head, 64-row block).  The 4 units of a workgroup belong to one KV
-// head, so every K/V tile staged in LDS serves all of them.  K and V have
-// their own double buffers: K(t+1) and V(t) are issued by the A waves in phase
-// 2t (buffer_load ... lds) and waited for at the end of phase 2t+1, two phases
-// before their first use.  Units are numbered head-fastest within a KV head
-// (u = qb * G + head), 4 consecutive units per workgroup; workgroups run
-// longest causal range first, and KV heads are pinned to XCDs (workgroup i
-// runs on XCD i % 8) so a head's K/V stays in one L2.
+// head, so every K/V tile staged in LDS serves all of them.  K and V tiles
+// rotate through three LDS buffers each: in the window between barriers j-1
+// and j the products read K(j) and V(j-1), and the A waves issue K(j+2) and
+// V(j+1) (buffer_load ... lds), which must land by barriers j+1 and j+1; the
+// buffer each overwrites was last read two windows earlier.  Units are
+// numbered head-fastest within a KV head (u = qb * G + head), 4 consecutive
+// units per workgroup; workgroups run longest causal range first, and KV heads
+// are pinned to XCDs (workgroup i runs on XCD i % 8) so a head's K/V stays in
+// one L2.
 #include "attn_common.h"
 
 namespace qfa {
 
+#ifndef QFA_PREFILL_BUFFERS
+#define QFA_PREFILL_BUFFERS 3
+#endif
+constexpr int kPrefillBuffers = QFA_PREFILL_BUFFERS;
+static_assert(kPrefillBuffers == 3 || kPrefillBuffers == 4, "3 or 4 LDS buffers per operand");
+
+__device__ __forceinline__ void wait_lgkm_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+
+// vmcnt(n) for a wave-uniform n in [0, 16]: waits until at most n of this
+// wave's vector-memory loads are outstanding.
+__device__ __forceinline__ void wait_vmem_le(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    case 15: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+    default: __builtin_amdgcn_s_waitcnt(0x4F70); break;  // 16: vmcnt bits 5:4 live in simm16 bits 15:14
+  }
+}
+
 // Workgroup barrier without a memory fence: the waits the schedule needs
 // (DMA completion, LDS stores) are explicit.  The scheduler does not move
-// instructions across it, which keeps the two phases apart.
-__device__ __forceinline__ void phase_barrier() {
+// instructions across it.
+__device__ __forceinline__ void window_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ void wait_lgkm_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
-
 template <int D, bool COMP>
 __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) {
   using TL = TileLayout<D>;
+  constexpr int NB = kPrefillBuffers;  // LDS buffers per operand
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar control flow
-  const int pair = wave & 3, half = wave >> 2;
+  // half 0 (rows 0..31 of a unit) runs products then softmax in a window,
+  // half 1 (rows 32..63) softmax then products.  Waves 0..3 (the older wave of
+  // each SIMD) take half 1.  Measured on MI355X: the products of the younger
+  // wave of a SIMD can run up to twice as long beside the older wave's
+  // softmax, whatever the issue priorities, and this assignment is about 3%
+  // faster than the reverse one.
+  const int pair = wave & 3, half = 1 - (wave >> 2);
   const int n = lane & 31;
 
   // ---- workgroup -> (KV group, rank): longest first, groups pinned to XCDs
@@ -98,66 +144,88 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   const int jlim = a.causal ? min(i + off, L - 1) : (L - 1);
   const int jmin_w = a.causal ? (i0 + off) : (L - 1);  // smallest limit over the wave's rows
 
-  uint8_t* kbuf = smem;                 // 2 x K region
-  uint8_t* vbuf = smem + 2 * TL::KREG;  // 2 x V region
-  float* dl = reinterpret_cast<float*>(smem + 2 * (TL::KREG + TL::VREG)) + wave * 32 * 32;
+  uint8_t* kbuf = smem;                                   // NB x K region
+  uint8_t* vbuf = smem + NB * TL::KREG;                   // NB x V region
+  uint8_t* trash = smem + NB * (TL::KREG + TL::VREG);     // 1 KB sink of unused DMA slots
+  float* dl = reinterpret_cast<float*>(trash + 1024) + wave * 32 * 32;
 
-  // Both buffer pairs start zeroed: bytes a ragged tile does not cover then hold
+  // All buffers start zeroed: bytes a ragged tile does not cover then hold
   // zeros or codes of an earlier tile, never uninitialised (possibly NaN) codes.
-  for (int o = threadIdx.x * 16; o < 2 * (TL::KREG + TL::VREG); o += blockDim.x * 16)
+  for (int o = threadIdx.x * 16; o < NB * (TL::KREG + TL::VREG); o += blockDim.x * 16)
     *reinterpret_cast<uint4*>(smem + o) = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
-  TileLoader<D, 4> ld;
-  ld.init(a.k4, a.k4s, a.v8, a.v8s, (size_t)grp, L, L, pair);
+  TileLoader<D, 8> ld;  // all 8 waves share the DMA
+  ld.init(a.k4, a.k4s, a.v8, a.v8s, (size_t)grp, L, L, wave);
   LaneOffs<D> lo;
   lo.init();
-  if (half == 0 && T > 0) ld.issue_k(0, kbuf, pair);
-  wait_vmem_all();
-  if (wave == 0 && T > 0) {
-    ld.fixup(0, kbuf);
+  constexpr int SLOTS = TileLoader<D, 8>::SLOTS;  // code DMA instructions per wave and window
+  // K(0 .. NB-2), V(0 .. NB-3) before the loop
+  for (int j = 0; j < NB - 1 && j < T; ++j) ld.issue_k(j, kbuf + j * TL::KREG, wave);
+  for (int j = 0; j < NB - 2 && j < T; ++j) ld.issue_v(j, vbuf + j * TL::VREG, wave);
+  wait_vmem_le(0);
+  __syncthreads();  // every wave's loads have landed before the scale patch
+  if (wave == 0) {
+    for (int j = 0; j < NB - 1 && j < T; ++j) ld.fixup(j, kbuf + j * TL::KREG);
     wait_lgkm_all();
   }
   __syncthreads();
 
-  v8i pb[2];  // P of the last softmax, consumed by the next MFMA phase
+  v8i pb[2];  // P of the last softmax, consumed by the next products
   int pscale = kScaleOne;
-  if (half == 1) phase_barrier();  // B runs one phase behind A
+  int kb_cur = 0, vb_prev = NB - 1;  // buffer of K(t) and of V(t-1)
+  int issued_prev = 0;               // DMA loads this wave issued one window ago
+#pragma nounroll
   for (int t = 0; t <= T; ++t) {
-    // ---- MFMA phase: P V of tile t-1 and S of tile t; A waves also issue K(t+1), V(t)
-    if (half == 0) {
-      if (t + 1 < T) ld.issue_k(t + 1, kbuf + ((t + 1) & 1) * TL::KREG, pair);
-      if (t < T) ld.issue_v(t, vbuf + (t & 1) * TL::VREG, pair);
-    }
+    // ---- DMA of K(t+NB-1) and V(t+NB-2) into the buffers last read in the
+    // previous window (tile j lives in buffer j % NB): the scale loads here,
+    // the code loads one per MFMA step of the products, spread over all waves
+    const bool dk = t + NB - 1 < T, dv = t + NB - 2 < T;
+    uint8_t* kdst = kbuf + (kb_cur == 0 ? NB - 1 : kb_cur - 1) * TL::KREG;
+    int vb2 = vb_prev + NB - 1;
+    vb2 -= vb2 >= NB ? NB : 0;
+    uint8_t* vdst = vbuf + vb2 * TL::VREG;
+    const int issued = SLOTS + ld.issue_scales(t + NB - 1, kdst, dk, t + NB - 2, vdst, dv, wave);
+    auto dma = [&](int k) { ld.dma_slot(k, t + NB - 1, kdst, dk, t + NB - 2, vdst, dv, wave, trash); };
+    // ---- products of tile t at raised priority: P V(t-1), then S(t) = K(t) Q^T
     const bool do_pv = t >= 1 && t - 1 < Tw, do_qk = t < Tw;
     v16f s[4];  // S of tile t: written here, consumed by this iteration's softmax
     if (COMP && do_qk && (t & 31) == 0)
       compute_delta<D>(dl, a.kbar + (size_t)grp * ntk * D, ntk, t, a.qbf + (((size_t)b * a.Hq + h) * Sq + i0) * D, D,
                        Sq - i0);
-    // all LDS operand reads first, then the products back to back
-    // (a wave's last P V also computes a product of whatever K buffer t & 1
+    __builtin_amdgcn_s_setprio(2);
+    // (a wave's last P V also computes a product of whatever K buffer kb_cur
     // holds; that S is never used: one code path keeps the register budget)
     if (do_pv) {
-      pv_then_qk<D>(st, lo, vbuf + ((t - 1) & 1) * TL::VREG, pb, pscale, kbuf + (t & 1) * TL::KREG, s);
-    } else if (do_qk) {
-      qk_tile<D>(st, lo, kbuf + (t & 1) * TL::KREG, s);
+      pv_then_qk<D>(st, lo, vbuf + vb_prev * TL::VREG, pb, pscale, kbuf + kb_cur * TL::KREG, s, dma);
+    } else {
+#pragma unroll
+      for (int k = 0; k < SLOTS; ++k) dma(k);
+      if (do_qk) qk_tile<D>(st, lo, kbuf + kb_cur * TL::KREG, s);
     }
-    phase_barrier();
-    // ---- softmax phase of tile t; A waves then wait for the DMA issued above
+    __builtin_amdgcn_s_setprio(0);
+    // ---- end of this wave's window: its loads of K(t+1) and V(t) (issued
+    // NB-2 windows ago) have landed, the K-scale patch of K(t+1) is written
+    // by the wave that loaded those scales, then the barrier
+    auto end_window = [&]() {
+      wait_vmem_le(issued + (NB - 3) * issued_prev);
+      if (wave == 0 && t + 1 < T) {
+        ld.fixup(t + 1, kbuf + (kb_cur + 1 == NB ? 0 : kb_cur + 1) * TL::KREG);
+        wait_lgkm_all();
+      }
+      window_barrier();
+    };
+    if (half == 1) end_window();
+    // ---- softmax of tile t
     if (t < Tw) {
       const float d32 = COMP ? a.c2 * dl[(t & 31) * 32 + n] : 0.0f;
       const bool need_mask = (kTile * t + kTile - 1 > jmin_w) || (kTile * t + kTile > L);
       softmax_tile<D, COMP>(st, s, t, need_mask, jlim, d32, pb, pscale);
     }
-    if (half == 0) {
-      wait_vmem_all();
-      if (wave == 0 && t + 1 < T) {
-        ld.fixup(t + 1, kbuf + ((t + 1) & 1) * TL::KREG);
-        wait_lgkm_all();
-      }
-    }
-    phase_barrier();
+    if (half == 0) end_window();
+    issued_prev = issued;
+    kb_cur = kb_cur + 1 == NB ? 0 : kb_cur + 1;
+    vb_prev = vb_prev + 1 == NB ? 0 : vb_prev + 1;
   }
-  if (half == 0) phase_barrier();  // A matches B's extra leading barrier
 
   if (rvalid) store_row<D>(st, a.O + qrow * D, a.lse ? a.lse + qrow : nullptr);
 }
@@ -170,7 +238,7 @@ static hipError_t prefill_d(const AttnArgs& a, hipStream_t s) {
   const long long nwg = (long long)a.B * a.Hkv * nwg_per_group;
   if (nwg == 0) return hipSuccess;
   const bool comp = a.kbar != nullptr;
-  const size_t lds = 2 * (TL::KREG + TL::VREG) + (comp ? (size_t)8 * 32 * 32 * 4 : 0);
+  const size_t lds = kPrefillBuffers * (TL::KREG + TL::VREG) + 1024 + (comp ? (size_t)8 * 32 * 32 * 4 : 0);
   if (comp)
     hipLaunchKernelGGL((k_prefill<D, true>), dim3((unsigned)nwg), dim3(512), lds, s, a, nwg_per_group);
   else

@@ -75,6 +75,7 @@ CASES = [
     (1, 16, 2, 45, 1000, 128, False, False, 0.0, "noncausal-G8"),
     (1, 12, 1, 200, 200, 128, True, False, 0.0, "G12-two-head-chunks"),
     (2, 4, 4, 130, 130, 64, True, True, 3.0, "batch2-comp-D64"),
+    (1, 2, 1, 129, 1001, 64, True, False, 0.0, "odd-keys-D64-8tiles"),
 ]
 
 
