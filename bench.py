@@ -48,6 +48,7 @@ def parse():
 
 COPY_BYTES = 1 << 30
 CPU_TARGET_S = 15.0
+MAX_CPU_ROWS = 131072  # bounded CPU sample: at most a quarter of llama16k's 524288 rows
 
 
 def run_copy(args):
@@ -262,9 +263,9 @@ def main():
         n_rows = 64
         while True:
             dt, pairs = sample(n_rows)
-            if dt >= CPU_TARGET_S / 2 or n_rows >= 16384:
+            if dt >= CPU_TARGET_S / 2 or n_rows >= MAX_CPU_ROWS:
                 break
-            n_rows = int(min(16384, n_rows * min(16.0, CPU_TARGET_S / max(dt, 1e-3))))
+            n_rows = int(min(MAX_CPU_ROWS, n_rows * min(16.0, CPU_TARGET_S / max(dt, 1e-3))))
         cpu_tflops = 4.0 * D * pairs / dt / 1e12
         out["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
                                "kind": "oracle",
