@@ -183,22 +183,24 @@ struct TileLoader {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(e ? vreg + ins * 1024 : trash), 16, vv, 0, 0, 0);
     }
   }
-  // Scale instructions of a tile pair: wave i < NKS loads K-scale dword block
-  // i, wave NKS the V scales; returns how many loads this wave issued.
-  __device__ __forceinline__ int issue_scales(int tk, uint8_t* kreg, bool ek, int tv, uint8_t* vreg, bool ev,
-                                              int wave) const {
+  // The scale bytes of a tile pair as dword loads of 256 B, one per wave:
+  // waves 0 .. NKS-1 the K-scale blocks, the next NVS waves the V-scale
+  // blocks, every other wave (or an unwanted tile) a load of nothing into
+  // `trash`.  Branch-free like dma_slot.
+  static constexpr int NVS = TL::VS_BYTES / 256;
+  __device__ __forceinline__ void scale_slot(int tk, uint8_t* kreg, bool ek, int tv, uint8_t* vreg, bool ev,
+                                             int wave, uint8_t* trash) const {
+    static_assert(TL::NKS + NVS <= NW, "one scale load per wave");
     const int lane = threadIdx.x & 63;
-    if (ek && wave < TL::NKS) {
-      const __amdgpu_buffer_rsrc_t r = rsrc_at(ks, ks_bytes, (uint32_t)tk * TL::KS_BYTES + wave * 256);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(kreg + TL::KC + wave * 256), 4, lane * 4, 0, 0, 0);
-      return 1;
-    }
-    if (ev && wave == TL::NKS) {
-      const __amdgpu_buffer_rsrc_t r = rsrc_at(vs, vs_bytes, (uint32_t)tv * TL::VS_BYTES);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(vreg + TL::VC), 16, lane * 16, 0, 0, 0);
-      return 1;
-    }
-    return 0;
+    const bool isk = wave < TL::NKS, isv = !isk && wave < TL::NKS + NVS;
+    const int i = isk ? wave : (isv ? wave - TL::NKS : 0);
+    const bool e = (isk && ek) || (isv && ev);
+    const uint8_t* base = isk ? ks : vs;
+    const uint32_t bytes = e ? (isk ? ks_bytes : vs_bytes) : 0u;
+    const uint32_t off = (uint32_t)(isk ? tk * TL::KS_BYTES : tv * TL::VS_BYTES) + i * 256;
+    uint8_t* dst = !e ? trash : (isk ? kreg + TL::KC : vreg + TL::VC) + i * 256;
+    const __amdgpu_buffer_rsrc_t r = rsrc_at(base, bytes, off);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, lane * 4, 0, 0, 0);
   }
 
   // D = 64 with an odd key count: the last token's two scale bytes share a

@@ -173,19 +173,24 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   v8i pb[2];  // P of the last softmax, consumed by the next products
   int pscale = kScaleOne;
   int kb_cur = 0, vb_prev = NB - 1;  // buffer of K(t) and of V(t-1)
-  int issued_prev = 0;               // DMA loads this wave issued one window ago
 #pragma nounroll
   for (int t = 0; t <= T; ++t) {
     // ---- DMA of K(t+NB-1) and V(t+NB-2) into the buffers last read in the
-    // previous window (tile j lives in buffer j % NB): the scale loads here,
-    // the code loads one per MFMA step of the products, spread over all waves
+    // previous window (tile j lives in buffer j % NB): one load per MFMA step
+    // of the products, the same count on every wave (one scale slot, then the
+    // code slots)
     const bool dk = t + NB - 1 < T, dv = t + NB - 2 < T;
     uint8_t* kdst = kbuf + (kb_cur == 0 ? NB - 1 : kb_cur - 1) * TL::KREG;
     int vb2 = vb_prev + NB - 1;
     vb2 -= vb2 >= NB ? NB : 0;
     uint8_t* vdst = vbuf + vb2 * TL::VREG;
-    const int issued = SLOTS + ld.issue_scales(t + NB - 1, kdst, dk, t + NB - 2, vdst, dv, wave);
-    auto dma = [&](int k) { ld.dma_slot(k, t + NB - 1, kdst, dk, t + NB - 2, vdst, dv, wave, trash); };
+    constexpr int issued = SLOTS + 1;  // loads per wave and window: the code slots and one scale slot
+    auto dma = [&](int k) {
+      if (k == 0)
+        ld.scale_slot(t + NB - 1, kdst, dk, t + NB - 2, vdst, dv, wave, trash);
+      else if (k <= SLOTS)
+        ld.dma_slot(k - 1, t + NB - 1, kdst, dk, t + NB - 2, vdst, dv, wave, trash);
+    };
     // ---- products of tile t at raised priority: P V(t-1), then S(t) = K(t) Q^T
     const bool do_pv = t >= 1 && t - 1 < Tw, do_qk = t < Tw;
     v16f s[4];  // S of tile t: written here, consumed by this iteration's softmax
@@ -199,7 +204,7 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
       pv_then_qk<D>(st, lo, vbuf + vb_prev * TL::VREG, pb, pscale, kbuf + kb_cur * TL::KREG, s, dma);
     } else {
 #pragma unroll
-      for (int k = 0; k < SLOTS; ++k) dma(k);
+      for (int k = 0; k <= SLOTS; ++k) dma(k);
       if (do_qk) qk_tile<D>(st, lo, kbuf + kb_cur * TL::KREG, s);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -207,7 +212,7 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
     // NB-2 windows ago) have landed, the K-scale patch of K(t+1) is written
     // by the wave that loaded those scales, then the barrier
     auto end_window = [&]() {
-      wait_vmem_le(issued + (NB - 3) * issued_prev);
+      wait_vmem_le((NB - 2) * issued);
       if (wave == 0 && t + 1 < T) {
         ld.fixup(t + 1, kbuf + (kb_cur + 1 == NB ? 0 : kb_cur + 1) * TL::KREG);
         wait_lgkm_all();
@@ -222,7 +227,6 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
       softmax_tile<D, COMP>(st, s, t, need_mask, jlim, d32, pb, pscale);
     }
     if (half == 0) end_window();
-    issued_prev = issued;
     kb_cur = kb_cur + 1 == NB ? 0 : kb_cur + 1;
     vb_prev = vb_prev + 1 == NB ? 0 : vb_prev + 1;
   }
