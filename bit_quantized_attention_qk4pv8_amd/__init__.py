@@ -171,11 +171,15 @@ def quantize_v8(v: torch.Tensor, stream=None):
 
 def fwd_prefill(q4, q4s, k4, k4s, v8, v8s, S_kv: int, causal: bool, softmax_scale: float, kbar=None,
                 q_bf16=None, with_lse: bool = True, stream=None):
-    B, Hq, S_q, Dh = q4.shape
-    D = Dh * 2
+    """q4/q4s None: the kernel quantises q_bf16 [B,Hq,S_q,D] itself."""
+    if q4 is None:
+        B, Hq, S_q, D = q_bf16.shape
+    else:
+        B, Hq, S_q, Dh = q4.shape
+        D = Dh * 2
     Hkv = k4.shape[1]
-    O = torch.empty((B, Hq, S_q, D), dtype=torch.float32, device=q4.device)
-    lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=q4.device) if with_lse else None
+    O = torch.empty((B, Hq, S_q, D), dtype=torch.float32, device=k4.device)
+    lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=k4.device) if with_lse else None
     qfa_fwd_prefill(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_q, S_kv, D, causal, softmax_scale, 32,
                     O, lse, stream)
     return O, lse
@@ -183,16 +187,20 @@ def fwd_prefill(q4, q4s, k4, k4s, v8, v8s, S_kv: int, causal: bool, softmax_scal
 
 def fwd_decode(q4, q4s, k4, k4s, v8, v8s, S_kv_max: int, softmax_scale: float, num_splits: int = 0,
                kv_lens=None, kbar=None, q_bf16=None, workspace=None, stream=None):
-    """q4 [B,Hq,1,D/2]; returns (O [B,Hq,D], lse [B,Hq], splits used)."""
-    B, Hq, _, Dh = q4.shape
-    D = Dh * 2
+    """q4 [B,Hq,1,D/2] (or None: the kernel quantises q_bf16 [B,Hq,1,D]);
+    returns (O [B,Hq,D], lse [B,Hq], splits used)."""
+    if q4 is None:
+        B, Hq, _, D = q_bf16.shape
+    else:
+        B, Hq, _, Dh = q4.shape
+        D = Dh * 2
     Hkv = k4.shape[1]
     splits = num_splits if num_splits > 0 else qfa_decode_default_splits(B, Hkv, S_kv_max)
     nbytes = qfa_decode_workspace_bytes(B, Hq, D, splits)
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q4.device)
-    O = torch.empty((B, Hq, D), dtype=torch.float32, device=q4.device)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=q4.device)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=k4.device)
+    O = torch.empty((B, Hq, D), dtype=torch.float32, device=k4.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=k4.device)
     used = qfa_fwd_decode(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D,
                           softmax_scale, 32, splits, workspace, workspace.numel(), O, lse, stream)
     return O, lse, used

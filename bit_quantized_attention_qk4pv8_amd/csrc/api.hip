@@ -76,12 +76,17 @@ static qfa_status check_attn_common(const uint8_t* q4, const uint8_t* q4s, const
   if (block_size != 32 || !attn_dim_ok(D)) return QFA_ERR_UNSUPPORTED;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return QFA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return QFA_ERR_INVALID_ARG;
-  if ((kbar == nullptr) != (q_bf16 == nullptr)) return QFA_ERR_INVALID_ARG;
-  const void* ptrs[] = {q4, k4, v8, O};
+  // Q comes quantised (q4 and q4s) or as bf16 to be quantised in the kernel
+  // (both null, q_bf16 set); the compensation (kbar) also needs q_bf16.
+  if ((q4 == nullptr) != (q4s == nullptr)) return QFA_ERR_INVALID_ARG;
+  if ((q4 == nullptr || kbar != nullptr) && q_bf16 == nullptr) return QFA_ERR_INVALID_ARG;
+  const void* ptrs[] = {k4, v8, O};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return QFA_ERR_INVALID_ARG;
-  if (!q4s || !k4s || !v8s) return QFA_ERR_INVALID_ARG;
-  if (kbar && (!aligned16(kbar) || !aligned16(q_bf16))) return QFA_ERR_INVALID_ARG;
+  if (!k4s || !v8s) return QFA_ERR_INVALID_ARG;
+  if (q4 && !aligned16(q4)) return QFA_ERR_INVALID_ARG;
+  if (q_bf16 && !aligned16(q_bf16)) return QFA_ERR_INVALID_ARG;
+  if (kbar && !aligned16(kbar)) return QFA_ERR_INVALID_ARG;
   return QFA_OK;
 }
 

@@ -40,7 +40,8 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
 
   RowState<D> st;
   const size_t qrow = (size_t)b * a.Hq + (rvalid ? h : 0);
-  load_q<D>(st, a.q4 + qrow * (D / 2), a.q4s + qrow * (D / 32), rvalid);
+  load_q<D>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * (D / 32) : nullptr,
+            a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid);
 
   uint8_t* bufs = smem;
   float* dl = reinterpret_cast<float*>(smem + 2 * TL::STRIDE);

@@ -549,15 +549,33 @@ __device__ __forceinline__ void compute_delta(float* dl, const uint16_t* kbar_bg
 }
 
 // Q fragments of this lane's row (zeros when invalid) and a fresh row state.
+// With q4row null, the row is quantised here from its bf16 values qbfrow
+// (times c2, then the MXFP4 block rule): the same bytes the quantiser kernel
+// writes for Q with prescale c2.
 template <int D>
-__device__ __forceinline__ void load_q(RowState<D>& st, const uint8_t* q4row, const uint8_t* q4srow, bool valid) {
+__device__ __forceinline__ void load_q(RowState<D>& st, const uint8_t* q4row, const uint8_t* q4srow,
+                                       const uint16_t* qbfrow, float c2, bool valid) {
   const int g = (threadIdx.x & 63) >> 5;
   st.qs = 0;
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) {
     const int b = kblock<D>(g, k);
-    st.qa[k] = valid ? *reinterpret_cast<const v4i*>(q4row + 16 * b) : v4i{0, 0, 0, 0};
-    st.qs |= (valid ? (int)q4srow[b] : 0) << (8 * k);
+    if (!valid) {
+      st.qa[k] = v4i{0, 0, 0, 0};
+    } else if (q4row) {
+      st.qa[k] = *reinterpret_cast<const v4i*>(q4row + 16 * b);
+      st.qs |= (int)q4srow[b] << (8 * k);
+    } else {
+      float v[kBlock];
+      load_bf16_block(qbfrow + kBlock * b, v);
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) v[i] = v[i] * c2;
+      uint4 c;
+      uint8_t sc;
+      mxfp4_block(v, c, sc);
+      st.qa[k] = v4i{(int)c.x, (int)c.y, (int)c.z, (int)c.w};
+      st.qs |= (int)sc << (8 * k);
+    }
   }
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) st.o[cb] = v16f{};

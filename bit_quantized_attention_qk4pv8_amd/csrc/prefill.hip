@@ -140,7 +140,8 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   const int i = i0 + n;
   const bool rvalid = wave_active && i < Sq;
   const size_t qrow = ((size_t)b * a.Hq + h) * Sq + (rvalid ? i : 0);
-  load_q<D>(st, a.q4 + qrow * (D / 2), a.q4s + qrow * (D / 32), rvalid);
+  load_q<D>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * (D / 32) : nullptr,
+            a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid);
   const int jlim = a.causal ? min(i + off, L - 1) : (L - 1);
   const int jmin_w = a.causal ? (i0 + off) : (L - 1);  // smallest limit over the wave's rows
 

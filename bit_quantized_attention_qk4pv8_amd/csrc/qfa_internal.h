@@ -44,6 +44,53 @@ __device__ __forceinline__ int mx_block_exponent(uint32_t amax_bits, int k) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// One MXFP4 block: 32 binary32 values -> 16 bytes of E2M1 codes (element 2k
+// in the low nibble of byte k, RNE by the hardware converter on the exact
+// x * 2^-e) and its E8M0 scale code (e + 127).  A block holding a non-finite
+// value gets scale 0xFF and zero codes.  Used by the quantiser kernel and by
+// the attention kernels that quantise Q themselves, so both produce the same
+// bytes.
+__device__ __forceinline__ void mxfp4_block(const float (&v)[kBlock], uint4& codes, uint8_t& scale) {
+  uint32_t amax = 0u, nonfinite = 0u;
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) {
+    const uint32_t a = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+    nonfinite |= (a >= 0x7F800000u);
+    amax = a > amax ? a : amax;
+  }
+  codes = make_uint4(0u, 0u, 0u, 0u);
+  scale = 0xFF;
+  if (nonfinite) return;
+  const int e = mx_block_exponent(amax, 2);
+  const float inv = exp2i(-e);  // e in [-127, 126] for finite binary32 input
+  uint32_t wd[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t r = 0u;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 0] * inv, v[q * 8 + 1] * inv, 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 2] * inv, v[q * 8 + 3] * inv, 1.0f, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 4] * inv, v[q * 8 + 5] * inv, 1.0f, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 6] * inv, v[q * 8 + 7] * inv, 1.0f, 3);
+    wd[q] = r;
+  }
+  codes = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  scale = (uint8_t)(e + 127);
+}
+
+// 32 consecutive bf16 values (64 bytes, 16-byte aligned) -> binary32.
+__device__ __forceinline__ void load_bf16_block(const uint16_t* src, float (&v)[kBlock]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 u = reinterpret_cast<const uint4*>(src)[q];
+    const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[q * 8 + 2 * k] = bf16_bits_to_float(wds[k] & 0xFFFFu);
+      v[q * 8 + 2 * k + 1] = bf16_bits_to_float(wds[k] >> 16);
+    }
+  }
+}
+
 // MFMA wrappers (gfx950 block-scaled f8f6f4).  Format codes: 0 = FP8 E4M3, 4 = FP4 E2M1.
 // 32x32x64: lane l supplies row (l % 32) and K-block (l / 32); the scale byte
 // (bits 7:0 of the scale operand) applies to that lane's 32-element K-block.
@@ -78,7 +125,7 @@ struct AttnArgs {
   const uint8_t* v8;
   const uint8_t* v8s;
   const uint16_t* kbar;   // may be null
-  const uint16_t* qbf;    // may be null (null iff kbar null)
+  const uint16_t* qbf;    // bf16 Q: for the compensation and, when q4 is null, quantised in the kernel
   const int32_t* kv_lens; // decode only, may be null
   float* O;               // prefill: final O; decode: partial O workspace
   float* lse;             // prefill: final LSE (may be null); decode: partial LSE workspace

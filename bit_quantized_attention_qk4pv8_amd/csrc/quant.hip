@@ -62,18 +62,8 @@ __global__ void __launch_bounds__(256) k_quant_qk4(const uint16_t* __restrict__ 
   }
   for (int w = threadIdx.x; w < n * NB; w += blockDim.x) {
     const int j = w / NB, blk = w % NB;
-    const uint4* src = reinterpret_cast<const uint4*>(xs + (size_t)j * D + blk * kBlock);
     float v[kBlock];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint4 u = src[q];
-      uint32_t wds[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[q * 8 + 2 * k] = bf16_bits_to_float(wds[k] & 0xFFFFu);
-        v[q * 8 + 2 * k + 1] = bf16_bits_to_float(wds[k] >> 16);
-      }
-    }
+    load_bf16_block(xs + (size_t)j * D + blk * kBlock, v);
     if (smooth) {
 #pragma unroll
       for (int i = 0; i < kBlock; ++i) v[i] = v[i] - kb[blk * kBlock + i];
@@ -82,32 +72,10 @@ __global__ void __launch_bounds__(256) k_quant_qk4(const uint16_t* __restrict__ 
 #pragma unroll
       for (int i = 0; i < kBlock; ++i) v[i] = v[i] * prescale;
     }
-    uint32_t amax = 0u, nonfinite = 0u;
-#pragma unroll
-    for (int i = 0; i < kBlock; ++i) {
-      uint32_t a = __float_as_uint(v[i]) & 0x7FFFFFFFu;
-      nonfinite |= (a >= 0x7F800000u);
-      amax = a > amax ? a : amax;
-    }
     const size_t row = bh * (size_t)S + t0 + j;
-    uint4 out = {0u, 0u, 0u, 0u};
-    uint8_t sc = 0xFF;
-    if (!nonfinite) {
-      const int e = mx_block_exponent(amax, 2);
-      const float inv = exp2i(-e);  // e in [-127, 126] for finite binary32 input
-      uint32_t wd[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t r = 0u;
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 0] * inv, v[q * 8 + 1] * inv, 1.0f, 0);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 2] * inv, v[q * 8 + 3] * inv, 1.0f, 1);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 4] * inv, v[q * 8 + 5] * inv, 1.0f, 2);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[q * 8 + 6] * inv, v[q * 8 + 7] * inv, 1.0f, 3);
-        wd[q] = r;
-      }
-      out = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      sc = (uint8_t)(e + 127);
-    }
+    uint4 out;
+    uint8_t sc;
+    mxfp4_block(v, out, sc);
     *reinterpret_cast<uint4*>(codes + row * (D / 2) + blk * (kBlock / 2)) = out;
     scales[row * NB + blk] = sc;
   }

@@ -117,10 +117,16 @@ qfa_status qfa_quantize_v8(const uint16_t* v, int B, int H, int S, int D, int bl
  * binary32 value of the bf16 dot product.  S and P never reach memory.
  * Causal masks are bottom-right aligned: key j is visible to query i iff
  * j <= i + (S_kv - S_q); a row with no visible key gets O = 0, LSE = -inf.
- *   q4, q4s      MXFP4 Q [B][Hq][S_q][D/2], [B][Hq][S_q][D/32]
+ *   q4, q4s      MXFP4 Q [B][Hq][S_q][D/2], [B][Hq][S_q][D/32] -- or both NULL:
+ *                the kernel then quantises q_bf16 itself (each row read once,
+ *                times qfa_exp2_scale(softmax_scale), the MXFP4 block rule),
+ *                producing the same codes as qfa_quantize_qk4 and so the same
+ *                O and LSE, without the separate pass over Q (the "online
+ *                quantization" of the MpFA abstract, fused)
  *   k4, k4s      MXFP4 K [B][Hkv][S_kv][D/2], [..][D/32] (smoothed if kbar)
- *   kbar, q_bf16 both NULL (no compensation) or both set:
- *                kbar [B][Hkv][ceil(S_kv/128)][D] bf16, q_bf16 [B][Hq][S_q][D]
+ *   kbar         NULL (no compensation) or bf16 [B][Hkv][ceil(S_kv/128)][D]
+ *   q_bf16       bf16 Q [B][Hq][S_q][D]; required when kbar is set or q4 is
+ *                NULL, ignored otherwise
  *   v8, v8s      E4M3 V and its scales (layout above)
  *   O            out float32 [B][Hq][S_q][D];  lse out float32 [B][Hq][S_q] or NULL
  */
@@ -139,9 +145,10 @@ qfa_status qfa_fwd_prefill(const uint8_t* q4, const uint8_t* q4s, const uint8_t*
  * merges them: LSE = log sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s.  Runs
  * with no key get weight 0.  No causal mask.
  *   q4, q4s        MXFP4 Q [B][Hq][1][D/2], [B][Hq][1][D/32], quantised with
- *                  prescale qfa_exp2_scale(softmax_scale) as for prefill
+ *                  prescale qfa_exp2_scale(softmax_scale) as for prefill, or
+ *                  both NULL to have the kernel quantise q_bf16 (as for prefill)
  *   k4, k4s, v8, v8s   the pre-quantised KV cache, S_kv_max tokens per sequence
- *   kbar, q_bf16   both NULL or both set, as for prefill
+ *   kbar, q_bf16   as for prefill (q_bf16 [B][Hq][1][D])
  *   num_splits     in/out: 0 lets the library choose (written back); > 0 is used
  *   workspace      device buffer of at least qfa_decode_workspace_bytes(...)
  *   O, lse         out float32 [B][Hq][D], [B][Hq] (lse may be NULL)

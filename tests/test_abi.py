@@ -93,6 +93,19 @@ def test_validation_rejects_before_launch():
     assert pre(4, 2, 128, 32, fake, None, fake) == qfa.QFA_ERR_INVALID_ARG   # kbar without q_bf16
     assert pre(4, 2, 128, 32, None, None, None) == qfa.QFA_ERR_INVALID_ARG   # no output
     assert pre(4, 2, 128, 32, None, None, fake, scale=0.0) == qfa.QFA_ERR_INVALID_ARG
+    # Q quantised in the kernel: q4 and q4s both NULL, and q_bf16 (aligned) required
+    preq = lambda q4, q4s, qbf, kbar=None: _call_raw(
+        "qfa_fwd_prefill", q4, q4s, fake, fake, kbar, qbf, fake, fake, 1, 4, 2, 8, 8, 128, 1, F(0.125), 32, fake,
+        None, None)
+    assert preq(None, fake, fake) == qfa.QFA_ERR_INVALID_ARG      # q4 NULL but q4s given
+    assert preq(fake, None, fake) == qfa.QFA_ERR_INVALID_ARG      # q4s missing
+    assert preq(None, None, None) == qfa.QFA_ERR_INVALID_ARG      # no Q at all
+    assert preq(None, None, odd) == qfa.QFA_ERR_INVALID_ARG       # misaligned bf16 Q
+    assert preq(odd, fake, None) == qfa.QFA_ERR_INVALID_ARG       # misaligned codes
+    nsq = ctypes.c_int(1)
+    assert _call_raw("qfa_fwd_decode", None, None, fake, fake, None, None, fake, fake, 2, 8, 2, 1024, None, 128,
+                     F(0.1), 32, ctypes.byref(nsq), fake, ctypes.c_size_t(1 << 20), fake, None, None) == \
+        qfa.QFA_ERR_INVALID_ARG                                   # decode: no Q at all
     # decode: workspace too small is reported before launch
     ns = ctypes.c_int(4)
     st = _call_raw("qfa_fwd_decode", fake, fake, fake, fake, None, None, fake, fake, 2, 8, 2, 1024, None, 128,

@@ -32,22 +32,27 @@ def _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed, k_offset=0.0, q_scale=1.0):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
-def _gpu_prefill(q, k, v, causal, scale, smooth):
+def _gpu_prefill(q, k, v, causal, scale, smooth, fused=False):
+    """fused: Q goes in as bf16 and the prefill kernel quantises it (q4 = q4s = NULL)."""
     B, Hq, Sq, D = q.shape
     Skv = k.shape[2]
-    q4, q4s, _ = qfa.quantize_qk4(q, prescale=qfa.qfa_exp2_scale(scale))
+    if fused:
+        q4 = q4s = None
+    else:
+        q4, q4s, _ = qfa.quantize_qk4(q, prescale=qfa.qfa_exp2_scale(scale))
     k4, k4s, kbar = qfa.quantize_qk4(k, smooth=smooth)
     v8, v8s = qfa.quantize_v8(v)
     O, lse = qfa.fwd_prefill(q4, q4s, k4, k4s, v8, v8s, Skv, causal, scale, kbar=kbar,
-                             q_bf16=q if smooth else None)
+                             q_bf16=q if (smooth or fused) else None)
     torch.cuda.synchronize()
     return O, lse
 
 
-def _check_prefill(q, k, v, causal, scale, smooth, rows, label):
+def _check_prefill(q, k, v, causal, scale, smooth, rows, label, fused=False):
     B, Hq, Sq, D = q.shape
-    say("prefill", label, "q", tuple(q.shape), "k", tuple(k.shape), "causal", causal, "smooth", smooth)
-    O, lse = _gpu_prefill(q, k, v, causal, scale, smooth)
+    say("prefill", label, "q", tuple(q.shape), "k", tuple(k.shape), "causal", causal, "smooth", smooth,
+        "fused Q" if fused else "")
+    O, lse = _gpu_prefill(q, k, v, causal, scale, smooth, fused)
     res = oracle.prefill_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, causal, scale, smooth=smooth)
     Og = to_np(O)[rows[:, 0], rows[:, 1], rows[:, 2]]
     lg = to_np(lse)[rows[:, 0], rows[:, 1], rows[:, 2]]
@@ -98,6 +103,37 @@ def test_prefill_compensation_beyond_32_tiles():
     _check_prefill(q, k, v, False, 1 / math.sqrt(128), True, _all_rows(1, 2, 64), "comp-5000keys")
 
 
+FUSED_CASES = [
+    (1, 4, 2, 300, 300, 128, True, False, 0.0, "fused-causal-ragged-D128"),
+    (1, 5, 1, 70, 333, 64, True, False, 0.0, "fused-bottom-right-G5-D64"),
+    (1, 4, 1, 700, 700, 128, True, True, 3.0, "fused-compensation-causal"),
+    (2, 4, 4, 130, 130, 64, False, True, 3.0, "fused-batch2-comp-D64"),
+    (1, 2, 2, 100, 64, 128, True, False, 0.0, "fused-sq>skv-empty-rows"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[-1] for c in FUSED_CASES])
+def test_prefill_fused_q_matches_two_pass(case):
+    """Q quantised inside the prefill kernel gives the same bytes as the quantiser
+    pass, so O and LSE are bit-identical to the two-pass path."""
+    B, Hq, Hkv, Sq, Skv, D, causal, smooth, koff, label = case
+    q, k, v = _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed=zlib.crc32(label.encode()) % 1000, k_offset=koff, q_scale=2.0)
+    q[..., 0, :32] = 0.0                 # an all-zero Q block (scale code 0)
+    q[..., 1, 5] = 300.0                 # an outlier channel
+    say("prefill fused-vs-two-pass", label, tuple(q.shape), tuple(k.shape))
+    O1, l1 = _gpu_prefill(q, k, v, causal, 1.0 / math.sqrt(D), smooth)
+    O2, l2 = _gpu_prefill(q, k, v, causal, 1.0 / math.sqrt(D), smooth, fused=True)
+    assert torch.equal(O1, O2), label
+    assert torch.equal(l1, l2), label
+
+
+def test_prefill_fused_q_workload_vs_oracle():
+    w = WORKLOADS["llama16k"]
+    inp = make_inputs(w, seed=0)
+    rows = sample_rows(1, w.Hq, w.S_q, 256, seed=3, must=(0, 127, 128, 16383))
+    _check_prefill(inp["q"], inp["k"], inp["v"], w.causal, w.scale, w.smooth, rows, "llama16k-fused-q", fused=True)
+
+
 def test_prefill_deterministic():
     q, k, v = _rand_inputs(1, 4, 2, 300, 300, 128, seed=5)
     O1, l1 = _gpu_prefill(q, k, v, True, 0.088, False)
@@ -114,15 +150,18 @@ def test_prefill_workload_sampled(name, nrows):
 
 
 # ----------------------------------------------------------------------------- decode
-def _gpu_decode(q, k, v, num_splits, kv_lens=None, smooth=False):
+def _gpu_decode(q, k, v, num_splits, kv_lens=None, smooth=False, fused=False):
     B, Hq, _, D = q.shape
     Smax = k.shape[2]
-    q4, q4s, _ = qfa.quantize_qk4(q, prescale=qfa.qfa_exp2_scale(1 / math.sqrt(D)))
+    if fused:
+        q4 = q4s = None
+    else:
+        q4, q4s, _ = qfa.quantize_qk4(q, prescale=qfa.qfa_exp2_scale(1 / math.sqrt(D)))
     k4, k4s, kbar = qfa.quantize_qk4(k, smooth=smooth)
     v8, v8s = qfa.quantize_v8(v)
     lens = None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32, device="cuda")
     O, lse, used = qfa.fwd_decode(q4, q4s, k4, k4s, v8, v8s, Smax, 1 / math.sqrt(D), num_splits=num_splits,
-                                  kv_lens=lens, kbar=kbar, q_bf16=q if smooth else None)
+                                  kv_lens=lens, kbar=kbar, q_bf16=q if (smooth or fused) else None)
     torch.cuda.synchronize()
     return O, lse, used
 
@@ -193,3 +232,13 @@ def test_decode_workload_sampled_sequences():
     used = _check_decode(inp["q"], inp["k"], inp["v"], w.num_splits, label="decode-B64",
                          seqs=[0, 17, 42, 63])
     assert used == 16
+
+
+@pytest.mark.parametrize("smooth", [False, True])
+def test_decode_fused_q_matches_two_pass(smooth):
+    q, k, v = _rand_inputs(3, 8, 2, 1, 1000, 128, seed=21, q_scale=2.0, k_offset=3.0 if smooth else 0.0)
+    say("decode fused-vs-two-pass smooth", smooth)
+    O1, l1, u1 = _gpu_decode(q, k, v, 3, kv_lens=[1000, 517, 0], smooth=smooth)
+    O2, l2, u2 = _gpu_decode(q, k, v, 3, kv_lens=[1000, 517, 0], smooth=smooth, fused=True)
+    assert u1 == u2 == 3
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)
