@@ -140,8 +140,6 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   const int i = i0 + n;
   const bool rvalid = wave_active && i < Sq;
   const size_t qrow = ((size_t)b * a.Hq + h) * Sq + (rvalid ? i : 0);
-  load_q<D>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * (D / 32) : nullptr,
-            a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid);
   const int jlim = a.causal ? min(i + off, L - 1) : (L - 1);
   const int jmin_w = a.causal ? (i0 + off) : (L - 1);  // smallest limit over the wave's rows
 
@@ -160,9 +158,12 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   LaneOffs<D> lo;
   lo.init();
   constexpr int SLOTS = TileLoader<D, 8>::SLOTS;  // code DMA instructions per wave and window
-  // K(0 .. NB-2), V(0 .. NB-3) before the loop
+  // K(0 .. NB-2), V(0 .. NB-3) before the loop; Q (and its quantisation)
+  // while they are in flight
   for (int j = 0; j < NB - 1 && j < T; ++j) ld.issue_k(j, kbuf + j * TL::KREG, wave);
   for (int j = 0; j < NB - 2 && j < T; ++j) ld.issue_v(j, vbuf + j * TL::VREG, wave);
+  load_q<D>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * (D / 32) : nullptr,
+            a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid);
   wait_vmem_le(0);
   __syncthreads();  // every wave's loads have landed before the scale patch
   if (wave == 0) {
