@@ -82,10 +82,9 @@ struct TileLoader {
   uint32_t vk0, vk1, vkw, vv;                        // per-lane voffsets (vkw: K codes, parity of `wave`)
   int L;
 
-  // wave: index of the issuing wave when several waves split a tile (only its
-  // parity matters); 0 when one wave issues everything.
-  __device__ __forceinline__ void init(const uint8_t* k4, const uint8_t* k4s, const uint8_t* v8, const uint8_t* v8s,
-                                       size_t bg, int L_storage, int L_valid, int wave) {
+  // Point the loader at slice bg (a (batch, kv head) pair) of the K/V tensors.
+  __device__ __forceinline__ void slice(const uint8_t* k4, const uint8_t* k4s, const uint8_t* v8, const uint8_t* v8s,
+                                        size_t bg, int L_storage, int L_valid) {
     const int nvb_storage = (L_storage + 31) / 32, nvb = (L_valid + 31) / 32;
     L = L_valid;
     kc = k4 + bg * L_storage * (D / 2);
@@ -96,6 +95,13 @@ struct TileLoader {
     ks_bytes = (uint32_t)L_valid * (D / 32);
     vc_bytes = (uint32_t)nvb * D * 32;
     vs_bytes = (uint32_t)nvb * D;
+  }
+
+  // wave: index of the issuing wave when several waves split a tile (only its
+  // parity matters); 0 when one wave issues everything.
+  __device__ __forceinline__ void init(const uint8_t* k4, const uint8_t* k4s, const uint8_t* v8, const uint8_t* v8s,
+                                       size_t bg, int L_storage, int L_valid, int wave) {
+    slice(k4, k4s, v8, v8s, bg, L_storage, L_valid);
     const int p = threadIdx.x & 63;
     if (D == 128) {  // 16 tokens of 64 B per KB; kswz uses token bits 1, 2 and 4 (= KB parity)
       const int tl = p >> 2, kpos = p & 3;
@@ -110,11 +116,15 @@ struct TileLoader {
     vv = rl * 32 + 16 * (hpos ^ vswz(rl));
   }
 
-  // Resource for the bytes [off, ...) of a slice region.  A signed max has a
-  // scalar form (an unsigned saturating subtract would be VALU and make the
-  // descriptor divergent); both values are below 2^31.
+  // Resource for the bytes [off, bytes) of a slice region (empty when off >=
+  // bytes, whatever off is), so every access it allows lies inside the
+  // region.  The saturating subtract is written as two scalar instructions
+  // (the borrow of s_sub_u32 selects 0): left to the compiler it becomes a
+  // VALU clamp plus a readfirstlane in the middle of the MFMA sequence.
   static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const uint8_t* base, uint32_t bytes, uint32_t off) {
-    const int rem = __builtin_amdgcn_readfirstlane(max((int)bytes - (int)off, 0));
+    uint32_t r;
+    asm("s_sub_u32 %0, %1, %2\n\ts_cselect_b32 %0, 0, %0" : "=s"(r) : "s"(bytes), "s"(off) : "scc");
+    const int rem = (int)r;
     // raw buffer (stride 0): voffset + inst_offset >= rem reads as zero
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + off), (short)0, rem, 0x00020000);
   }
