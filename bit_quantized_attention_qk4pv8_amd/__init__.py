@@ -28,8 +28,8 @@ QFA_ERR_HIP = 4
 
 EXPORTS = (
     "qfa_quantize_qk4", "qfa_quantize_v8", "qfa_fwd_prefill", "qfa_fwd_decode",
-    "qfa_decode_workspace_bytes", "qfa_decode_default_splits", "qfa_exp2_scale", "qfa_status_string",
-    "qfa_version",
+    "qfa_decode_workspace_bytes", "qfa_decode_default_splits", "qfa_exp2_scale", "qfa_kv_append",
+    "qfa_status_string", "qfa_version",
 )
 
 _lib = None
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.qfa_decode_workspace_bytes.argtypes = [I, I, I, I]
         L.qfa_decode_default_splits.restype = I
         L.qfa_decode_default_splits.argtypes = [I, I, I]
+        L.qfa_kv_append.restype = I
+        L.qfa_kv_append.argtypes = [P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
         L.qfa_exp2_scale.restype = F
         L.qfa_exp2_scale.argtypes = [F]
         L.qfa_status_string.restype = ctypes.c_char_p
@@ -146,7 +148,35 @@ def qfa_fwd_decode(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max
     return ns.value
 
 
+def qfa_kv_append(k_new, v_new, B, Hkv, n_new, D, S_kv_max, block_size, kv_lens, k4, k4s, kbar, v8, v8s, k_tail,
+                  v_tail, stream=None):
+    _check("qfa_kv_append", lib().qfa_kv_append(
+        _ptr(_u16(k_new)), _ptr(_u16(v_new)), B, Hkv, n_new, D, S_kv_max, block_size, _ptr(kv_lens), _ptr(k4),
+        _ptr(k4s), _ptr(None if kbar is None else _u16(kbar)), _ptr(v8), _ptr(v8s),
+        _ptr(None if k_tail is None else _u16(k_tail)), _ptr(_u16(v_tail)), _stream(stream)))
+
+
 # ----------------------------------------------------------------------------- allocating helpers
+def kv_cache(B: int, Hkv: int, S_kv_max: int, D: int, smooth: bool = False, device="cuda"):
+    """Empty pre-quantised KV cache (the layouts qfa_fwd_decode reads) plus the bf16 tails
+    qfa_kv_append keeps between calls."""
+    nvb, nt = (S_kv_max + 31) // 32, (S_kv_max + 127) // 128
+    u8 = dict(dtype=torch.uint8, device=device)
+    c = {"k4": torch.zeros((B, Hkv, S_kv_max, D // 2), **u8), "k4s": torch.zeros((B, Hkv, S_kv_max, D // 32), **u8),
+         "v8": torch.zeros((B, Hkv, nvb, D, 32), **u8), "v8s": torch.zeros((B, Hkv, nvb, D), **u8),
+         "v_tail": torch.zeros((B, Hkv, 128, D), dtype=torch.bfloat16, device=device),
+         "kbar": None, "k_tail": None, "S": S_kv_max}
+    if smooth:
+        c["kbar"] = torch.zeros((B, Hkv, nt, D), dtype=torch.bfloat16, device=device)
+        c["k_tail"] = torch.zeros((B, Hkv, 128, D), dtype=torch.bfloat16, device=device)
+    return c
+
+
+def kv_append(cache, k_new: torch.Tensor, v_new: torch.Tensor, kv_lens=None, stream=None):
+    """Append bf16 k_new, v_new [B,Hkv,n,D] at kv_lens (device int32 [B] or None = empty cache)."""
+    B, Hkv, n, D = k_new.shape
+    qfa_kv_append(k_new, v_new, B, Hkv, n, D, cache["S"], 32, kv_lens, cache["k4"], cache["k4s"], cache["kbar"],
+                  cache["v8"], cache["v8s"], cache["k_tail"], cache["v_tail"], stream)
 def quantize_qk4(x: torch.Tensor, smooth: bool = False, prescale: float = 1.0, stream=None):
     """x bf16 [B,H,S,D] on the GPU -> (codes u8 [B,H,S,D/2], scales u8 [B,H,S,D/32], kbar bf16 or None).
 

@@ -114,6 +114,27 @@ qfa_status qfa_fwd_prefill(const uint8_t* q4, const uint8_t* q4s, const uint8_t*
   return from_hip(qfa::launch_prefill(a, stream));
 }
 
+qfa_status qfa_kv_append(const uint16_t* k_new, const uint16_t* v_new, int B, int Hkv, int n_new, int D,
+                         int S_kv_max, int block_size, const int32_t* kv_lens, uint8_t* k4, uint8_t* k4s,
+                         uint16_t* kbar, uint8_t* v8, uint8_t* v8s, uint16_t* k_tail, uint16_t* v_tail,
+                         hipStream_t stream) {
+  if (block_size != 32 || !qk_dim_ok(D)) return QFA_ERR_UNSUPPORTED;
+  if (B < 0 || Hkv < 0 || n_new < 0 || S_kv_max < 0 || (long long)B * Hkv > 65535) return QFA_ERR_INVALID_ARG;
+  if ((kbar == nullptr) != (k_tail == nullptr)) return QFA_ERR_INVALID_ARG;
+  if ((long long)B * Hkv * n_new == 0 || S_kv_max == 0) return QFA_OK;
+  const void* ptrs[] = {k_new, v_new, k4, v8, v_tail};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return QFA_ERR_INVALID_ARG;
+  if (!k4s || !v8s) return QFA_ERR_INVALID_ARG;
+  if (kbar && (!aligned16(kbar) || !aligned16(k_tail))) return QFA_ERR_INVALID_ARG;
+  qfa::AppendArgs a{};
+  a.k_new = k_new; a.v_new = v_new; a.kv_lens = kv_lens;
+  a.k4 = k4; a.k4s = k4s; a.kbar = kbar; a.v8 = v8; a.v8s = v8s;
+  a.k_tail = k_tail; a.v_tail = v_tail;
+  a.B = B; a.Hkv = Hkv; a.n = n_new; a.S = S_kv_max;
+  return from_hip(qfa::launch_kv_append(a, D, stream));
+}
+
 int qfa_decode_default_splits(int B, int Hkv, int S_kv_max) {
   const long long units = (long long)(B > 0 ? B : 1) * (Hkv > 0 ? Hkv : 1);
   const int tiles = S_kv_max > 0 ? (S_kv_max + 127) / 128 : 1;

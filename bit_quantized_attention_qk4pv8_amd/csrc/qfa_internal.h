@@ -136,6 +136,21 @@ struct AttnArgs {
 };
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);
+
+struct AppendArgs {
+  const uint16_t* k_new;   // bf16 [B][Hkv][n][D]
+  const uint16_t* v_new;
+  const int32_t* kv_lens;  // device int32 [B] (tokens already cached) or null (all 0)
+  uint8_t* k4;             // cache, S tokens per (b, kv head)
+  uint8_t* k4s;
+  uint16_t* kbar;          // null: no smoothing
+  uint8_t* v8;
+  uint8_t* v8s;
+  uint16_t* k_tail;        // bf16 [B][Hkv][128][D]; null iff kbar null
+  uint16_t* v_tail;        // bf16 [B][Hkv][128][D]
+  int B, Hkv, n, S;
+};
+hipError_t launch_kv_append(const AppendArgs& a, int D, hipStream_t s);
 hipError_t launch_decode(const AttnArgs& a, float* O, float* lse, hipStream_t s);
 
 }  // namespace qfa

@@ -81,6 +81,36 @@ __global__ void __launch_bounds__(256) k_quant_qk4(const uint16_t* __restrict__ 
   }
 }
 
+// One V record: the 32 token values of one channel (missing tokens 0) -> 32
+// E4M3 codes, RNE by the hardware converter on the exact x * 2^-e, and the
+// E8M0 code of e = ceil(log2 amax) - 8; a non-finite record gets scale 0xFF
+// and zero codes.  Shared by the V quantiser and the cache writer.
+__device__ __forceinline__ void fp8_block_store(const float (&x)[kBlock], uint8_t* dst, uint8_t* scale) {
+  uint32_t amax = 0u, nonfinite = 0u;
+#pragma unroll
+  for (int t = 0; t < kBlock; ++t) {
+    const uint32_t a = __float_as_uint(x[t]) & 0x7FFFFFFFu;
+    nonfinite |= (a >= 0x7F800000u);
+    amax = a > amax ? a : amax;
+  }
+  uint32_t wd[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  uint8_t sc = 0xFF;
+  if (!nonfinite) {
+    const int e = mx_block_exponent(amax, 8);
+    const float inv = exp2i(-e);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      int r = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q] * inv, x[4 * q + 1] * inv, 0, false);
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2] * inv, x[4 * q + 3] * inv, r, true);
+      wd[q] = (uint32_t)r;
+    }
+    sc = (uint8_t)(e + 127);
+  }
+  reinterpret_cast<uint4*>(dst)[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  reinterpret_cast<uint4*>(dst)[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+  *scale = sc;
+}
+
 // One workgroup per (b, h, 32-token block); thread c handles channel c.
 template <int D>
 __global__ void __launch_bounds__(D) k_quant_v8(const uint16_t* __restrict__ v, int S, int nblk,
@@ -98,31 +128,138 @@ __global__ void __launch_bounds__(D) k_quant_v8(const uint16_t* __restrict__ v, 
   __syncthreads();
   const int c = threadIdx.x;
   float x[kBlock];
-  uint32_t amax = 0u, nonfinite = 0u;
 #pragma unroll
-  for (int t = 0; t < kBlock; ++t) {
-    x[t] = (t < n) ? bf16_bits_to_float(tile[t * D + c]) : 0.0f;
-    uint32_t a = __float_as_uint(x[t]) & 0x7FFFFFFFu;
-    nonfinite |= (a >= 0x7F800000u);
-    amax = a > amax ? a : amax;
-  }
-  uint32_t wd[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  uint8_t sc = 0xFF;
-  if (!nonfinite) {
-    const int e = mx_block_exponent(amax, 8);
-    const float inv = exp2i(-e);
+  for (int t = 0; t < kBlock; ++t) x[t] = (t < n) ? bf16_bits_to_float(tile[t * D + c]) : 0.0f;
+  fp8_block_store(x, codes + ((bh * nblk + blk) * D + c) * kBlock, scales + (bh * nblk + blk) * D + c);
+}
+
+// ---------------------------------------------------------------- KV-cache writer
+// Appending n tokens to a sequence that holds L: the V records of the 32-token
+// blocks from floor(L/32) on and (with smoothing) every K row of the 128-token
+// tiles from floor(L/128) on are quantised again from raw bf16 values, which
+// for tokens below L come from the tail (the raw values of the sequence's
+// current partial 128-token tile), so the cache ends up with the bytes the
+// quantisers would write for the whole sequence at once.  Quantise-on-write:
+// hnwysp.cn MXAttention/MXFP4 notes, sections 3.4 and 5.4.
+
+// Valid range of sequence bg's append: tokens [L, L2), clamped to the cache.
+__device__ __forceinline__ void append_range(const AppendArgs& a, size_t bg, int& L, int& L2) {
+  const int b = (int)(bg / a.Hkv);
+  int l = a.kv_lens ? a.kv_lens[b] : 0;
+  l = min(max(l, 0), a.S);
+  L = l;
+  L2 = min(l + a.n, a.S);
+}
+
+// Raw bf16 row of token tau: the tail (base 128 floor(L/128)) below L, the new tokens from L.
+template <int D>
+__device__ __forceinline__ const uint16_t* tok_row(const uint16_t* tail, const uint16_t* nw, size_t bg, int n, int L,
+                                                   int tau) {
+  if (tau < L) return tail + (bg * kTile + (tau - (L / kTile) * kTile)) * D;
+  return nw + (bg * (size_t)n + (tau - L)) * D;
+}
+
+// One workgroup per (affected 32-token V block, sequence slice); thread c = channel c.
+template <int D>
+__global__ void __launch_bounds__(D) k_append_v(AppendArgs a) {
+  const size_t bg = blockIdx.y;
+  int L, L2;
+  append_range(a, bg, L, L2);
+  const int blk = L / kBlock + (int)blockIdx.x;
+  const int j0 = blk * kBlock;
+  if (j0 >= L2) return;
+  const int np = min(kBlock, L2 - j0);
+  const int c = threadIdx.x;
+  float x[kBlock];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      int r = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q] * inv, x[4 * q + 1] * inv, 0, false);
-      r = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2] * inv, x[4 * q + 3] * inv, r, true);
-      wd[q] = (uint32_t)r;
+  for (int t = 0; t < kBlock; ++t)
+    x[t] = (t < np) ? bf16_bits_to_float(tok_row<D>(a.v_tail, a.v_new, bg, a.n, L, j0 + t)[c]) : 0.0f;
+  const size_t nvb = (size_t)(a.S + kBlock - 1) / kBlock;
+  fp8_block_store(x, a.v8 + ((bg * nvb + blk) * D + c) * kBlock, a.v8s + (bg * nvb + blk) * D + c);
+}
+
+// One workgroup per (affected 128-token K tile, sequence slice): K-bar of the
+// tile's present tokens (smoothing), then the MXFP4 rows -- all of the tile's
+// rows when K-bar changed, else only the new ones.
+template <int D>
+__global__ void __launch_bounds__(256) k_append_k(AppendArgs a, int smooth) {
+  constexpr int NB = D / kBlock;
+  __shared__ float kb[D];
+  const size_t bg = blockIdx.y;
+  int L, L2;
+  append_range(a, bg, L, L2);
+  const int tile = L / kTile + (int)blockIdx.x;
+  const int t0 = tile * kTile;
+  if (t0 >= L2) return;
+  const int np = min(kTile, L2 - t0);
+  const int lo = smooth ? t0 : max(t0, L);
+  if (smooth) {
+    const size_t ntiles = (size_t)(a.S + kTile - 1) / kTile;
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+      double sum = 0.0;
+      for (int j = 0; j < np; ++j) sum += (double)bf16_bits_to_float(tok_row<D>(a.k_tail, a.k_new, bg, a.n, L, t0 + j)[c]);
+      const uint16_t bb = f64_to_bf16_rne(sum / (double)np);
+      kb[c] = bf16_bits_to_float(bb);
+      a.kbar[(bg * ntiles + tile) * D + c] = bb;
     }
-    sc = (uint8_t)(e + 127);
+    __syncthreads();
   }
-  uint8_t* dst = codes + ((bh * nblk + blk) * D + c) * kBlock;
-  reinterpret_cast<uint4*>(dst)[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-  reinterpret_cast<uint4*>(dst)[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
-  scales[(bh * nblk + blk) * D + c] = sc;
+  const int nrows = t0 + np - lo;
+  for (int w = threadIdx.x; w < nrows * NB; w += blockDim.x) {
+    const int j = lo + w / NB, blk = w % NB;
+    float v[kBlock];
+    load_bf16_block(tok_row<D>(a.k_tail, a.k_new, bg, a.n, L, j) + blk * kBlock, v);
+    if (smooth) {
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) v[i] = v[i] - kb[blk * kBlock + i];
+    }
+    uint4 out;
+    uint8_t sc;
+    mxfp4_block(v, out, sc);
+    const size_t row = bg * (size_t)a.S + j;
+    *reinterpret_cast<uint4*>(a.k4 + row * (D / 2) + blk * (kBlock / 2)) = out;
+    a.k4s[row * NB + blk] = sc;
+  }
+}
+
+// After the two kernels above: the tail takes the raw values of the new
+// partial tile's new tokens (its older tokens, if any, are already in place).
+template <int D>
+__global__ void __launch_bounds__(256) k_append_tail(AppendArgs a) {
+  const size_t bg = blockIdx.x;
+  int L, L2;
+  append_range(a, bg, L, L2);
+  const int base2 = (L2 / kTile) * kTile;
+  const int from = max(base2, L);
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  for (int w = threadIdx.x; w < (L2 - from) * CH; w += blockDim.x) {
+    const int tau = from + w / CH, ch = w % CH;
+    const size_t src = (bg * (size_t)a.n + (tau - L)) * D + ch * 8;
+    const size_t dst = (bg * kTile + (tau - base2)) * D + ch * 8;
+    *reinterpret_cast<uint4*>(a.v_tail + dst) = *reinterpret_cast<const uint4*>(a.v_new + src);
+    if (a.k_tail) *reinterpret_cast<uint4*>(a.k_tail + dst) = *reinterpret_cast<const uint4*>(a.k_new + src);
+  }
+}
+
+template <int D>
+static hipError_t append_d(const AppendArgs& a, hipStream_t s) {
+  const unsigned nbg = (unsigned)(a.B * a.Hkv);
+  const int smooth = a.kbar != nullptr;
+  hipLaunchKernelGGL(k_append_v<D>, dim3((unsigned)((a.n + kBlock - 1) / kBlock + 1), nbg), dim3(D), 0, s, a);
+  hipLaunchKernelGGL(k_append_k<D>, dim3((unsigned)((a.n + kTile - 1) / kTile + 1), nbg), dim3(256), 0, s, a, smooth);
+  hipLaunchKernelGGL(k_append_tail<D>, dim3(nbg), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const AppendArgs& a, int D, hipStream_t s) {
+  switch (D) {
+#define QFA_APPEND_CASE(DD) \
+  case DD: return append_d<DD>(a, s);
+    QFA_APPEND_CASE(32) QFA_APPEND_CASE(64) QFA_APPEND_CASE(96) QFA_APPEND_CASE(128) QFA_APPEND_CASE(160)
+    QFA_APPEND_CASE(192) QFA_APPEND_CASE(224) QFA_APPEND_CASE(256)
+#undef QFA_APPEND_CASE
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_quant_qk4(const uint16_t* x, int B, int H, int S, int D, int smooth, float prescale,

@@ -159,6 +159,35 @@ qfa_status qfa_fwd_decode(const uint8_t* q4, const uint8_t* q4s, const uint8_t* 
                           float softmax_scale, int block_size, int* num_splits, void* workspace,
                           size_t workspace_bytes, float* O, float* lse, hipStream_t stream);
 
+/*
+ * KV-cache writer: append n_new tokens to every sequence of a pre-quantised
+ * cache (quantise on write: hnwysp.cn MXAttention/MXFP4 notes, sections 3.4
+ * and 5.4; the cache feeds qfa_fwd_decode).  Sequence b holds L_b tokens
+ * (kv_lens: device int32 [B], or NULL for all 0) and receives tokens
+ * [L_b, L_b + n_new), clamped to S_kv_max; the caller advances kv_lens.
+ * Afterwards the cache holds, for tokens [0, L_b + n_new), exactly the bytes
+ * qfa_quantize_qk4 (K, smoothing as given) and qfa_quantize_v8 would write
+ * for the whole sequence: the V block of 32 tokens the append starts in is
+ * quantised again (its scale may change), and with smoothing so are all rows
+ * of the 128-token tile it starts in (K-bar changes).  Their earlier raw values
+ * come from the tails.
+ *   k_new, v_new   bf16 [B][Hkv][n_new][D]
+ *   k4, k4s, kbar  the K cache [B][Hkv][S_kv_max][D/2], [..][D/32],
+ *                  kbar [B][Hkv][ceil(S_kv_max/128)][D] or NULL (no smoothing)
+ *   v8, v8s        the V cache [B][Hkv][ceil(S_kv_max/32)][D][32], [..][D]
+ *   k_tail, v_tail bf16 [B][Hkv][128][D], caller-owned and kept between calls:
+ *                  the raw values of each sequence's last partial 128-token
+ *                  tile (rows 0 .. L_b - 128 floor(L_b/128) - 1 are read,
+ *                  the new partial tile's rows written).  k_tail is NULL iff
+ *                  kbar is NULL.  Start them with the cache: for L_b = 0
+ *                  nothing is read.
+ * Three kernels on `stream`; calls for the same cache must not overlap.
+ */
+qfa_status qfa_kv_append(const uint16_t* k_new, const uint16_t* v_new, int B, int Hkv, int n_new, int D,
+                         int S_kv_max, int block_size, const int32_t* kv_lens, uint8_t* k4, uint8_t* k4s,
+                         uint16_t* kbar, uint8_t* v8, uint8_t* v8s, uint16_t* k_tail, uint16_t* v_tail,
+                         hipStream_t stream);
+
 /* Bytes of decode workspace for the given shape and split count (> 0). */
 size_t qfa_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 

@@ -116,6 +116,21 @@ def test_validation_rejects_before_launch():
     assert st == qfa.QFA_ERR_INVALID_ARG
 
 
+def test_kv_append_validation():
+    P = ctypes.c_void_p
+    fake, odd = P(4096), P(4097)
+    app = lambda D=128, bs=32, n=4, kbar=None, ktail=None, knew=fake, vtail=fake: _call_raw(
+        "qfa_kv_append", knew, fake, 2, 2, n, D, 1024, bs, None, fake, fake, kbar, fake, fake, ktail, vtail, None)
+    assert app(bs=16) == qfa.QFA_ERR_UNSUPPORTED
+    assert app(D=48) == qfa.QFA_ERR_UNSUPPORTED
+    assert app(n=-1) == qfa.QFA_ERR_INVALID_ARG
+    assert app(kbar=fake) == qfa.QFA_ERR_INVALID_ARG          # smoothing needs the K tail
+    assert app(ktail=fake) == qfa.QFA_ERR_INVALID_ARG         # and the K tail needs smoothing
+    assert app(knew=odd) == qfa.QFA_ERR_INVALID_ARG           # misaligned input
+    assert app(vtail=None) == qfa.QFA_ERR_INVALID_ARG         # the V tail is always needed
+    assert app(n=0, knew=None) == qfa.QFA_OK                  # nothing to append
+
+
 def test_kv_cache_byte_formula_matches_printed_example():
     """Byte accounting used for the decode roofline reproduces the KV-cache
     formula example printed in the MXFP4 notes (section 1.1)."""

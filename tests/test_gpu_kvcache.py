@@ -1,0 +1,107 @@
+"""KV-cache writer (qfa_kv_append) on the GPU.
+
+Appending in chunks must leave exactly the bytes the quantisers write for the
+whole sequence at once (quantise on write: hnwysp.cn MXAttention/MXFP4 notes,
+sections 3.4 and 5.4): K codes and scales, K-bar with smoothing, V codes and
+scales, including the V block and the K-bar tile an append starts inside.
+Sequences of one batch have different lengths (kv_lens).  Decode on the
+appended cache equals decode on the one-shot cache, and one sequence is also
+checked against the oracle's quantisers.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_attention_qk4pv8_amd as qfa
+import oracle
+from bit_quantized_attention_qk4pv8_amd.workloads import bf16_bits
+from gpu_util import say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _data(B, Hkv, S, D, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    k = torch.randn((B, Hkv, S, D), generator=g, device="cuda")
+    k += torch.randn((B, Hkv, 1, D), generator=g, device="cuda") * 3.0   # channel offsets: K-bar matters
+    v = torch.randn((B, Hkv, S, D), generator=g, device="cuda")
+    v[:, :, 7, :] *= 50.0                                                 # an outlier token inside a V block
+    return k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def _sl(c, b):
+    return {k: (v[b:b + 1] if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
+
+
+def _check_against_one_shot(c, k, v, lens, smooth, label):
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        k4, k4s, kb = qfa.quantize_qk4(k[b:b + 1, :, :L].contiguous(), smooth=smooth)
+        v8, v8s = qfa.quantize_v8(v[b:b + 1, :, :L].contiguous())
+        nvb, nt = (L + 31) // 32, (L + 127) // 128
+        assert torch.equal(c["k4"][b:b + 1, :, :L], k4), (label, b, "K codes")
+        assert torch.equal(c["k4s"][b:b + 1, :, :L], k4s), (label, b, "K scales")
+        assert torch.equal(c["v8"][b:b + 1, :, :nvb], v8), (label, b, "V codes")
+        assert torch.equal(c["v8s"][b:b + 1, :, :nvb], v8s), (label, b, "V scales")
+        if smooth:
+            assert torch.equal(c["kbar"][b:b + 1, :, :nt], kb), (label, b, "K-bar")
+
+
+@pytest.mark.parametrize("D,smooth", [(128, True), (128, False), (64, True)])
+def test_append_in_chunks_equals_one_shot(D, smooth):
+    B, Hkv, S = 3, 2, 1200
+    k, v = _data(B, Hkv, S, D, seed=D + smooth)
+    c = qfa.kv_cache(B, Hkv, S, D, smooth=smooth)
+    lens = [0, 5, 200]
+    for b, L0 in enumerate(lens):          # different starting lengths, one sequence at a time
+        if L0:
+            qfa.kv_append(_sl(c, b), k[b:b + 1, :, :L0].contiguous(), v[b:b + 1, :, :L0].contiguous())
+    torch.cuda.synchronize()
+    _check_against_one_shot(c, k, v, lens, smooth, "start")
+    for n in (1, 31, 33, 128, 1, 97, 250, 3):   # chunks that start and end inside V blocks and K-bar tiles
+        say("kv_append D", D, "smooth", smooth, "lens", lens, "n", n)
+        kl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        kn = torch.stack([k[b, :, lens[b]:lens[b] + n] for b in range(B)]).contiguous()
+        vn = torch.stack([v[b, :, lens[b]:lens[b] + n] for b in range(B)]).contiguous()
+        qfa.kv_append(c, kn, vn, kv_lens=kl)
+        torch.cuda.synchronize()
+        lens = [L + n for L in lens]
+        _check_against_one_shot(c, k, v, lens, smooth, "after +%d" % n)
+
+
+def test_append_matches_oracle_and_feeds_decode():
+    B, Hkv, Hq, S, D = 2, 2, 8, 700, 128
+    k, v = _data(B, Hkv, S, D, seed=3)
+    c = qfa.kv_cache(B, Hkv, S, D, smooth=True)
+    lens = [0, 0]
+    for n in (100, 1, 130, 64, 2):
+        kl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        kn = torch.stack([k[b, :, lens[b]:lens[b] + n] for b in range(B)]).contiguous()
+        vn = torch.stack([v[b, :, lens[b]:lens[b] + n] for b in range(B)]).contiguous()
+        qfa.kv_append(c, kn, vn, kv_lens=kl)
+        lens = [L + n for L in lens]
+    torch.cuda.synchronize()
+    L = lens[0]
+    # the oracle's quantisers on the whole of sequence 1
+    oc, os_, ok = oracle.quantize_qk4(bf16_bits(k[1:2, :, :L]), smooth=True)
+    vc, vs = oracle.quantize_v8(bf16_bits(v[1:2, :, :L]))
+    nvb, nt = (L + 31) // 32, (L + 127) // 128
+    assert np.array_equal(to_np(c["k4"][1:2, :, :L]), oc)
+    assert np.array_equal(to_np(c["k4s"][1:2, :, :L]), os_)
+    assert np.array_equal(to_np(c["kbar"][1:2, :, :nt].view(torch.int16)).view(np.uint16), ok)
+    assert np.array_equal(to_np(c["v8"][1:2, :, :nvb]), vc)
+    assert np.array_equal(to_np(c["v8s"][1:2, :, :nvb]), vs)
+    # decode on the appended cache == decode on a cache quantised in one pass
+    g = torch.Generator(device="cuda").manual_seed(9)
+    q = torch.randn((B, Hq, 1, D), generator=g, device="cuda").to(torch.bfloat16)
+    kl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    O1, l1, _ = qfa.fwd_decode(None, None, c["k4"], c["k4s"], c["v8"], c["v8s"], S, 1 / math.sqrt(D), num_splits=3,
+                               kv_lens=kl, kbar=c["kbar"], q_bf16=q)
+    k4, k4s, kb = qfa.quantize_qk4(k[:, :, :L].contiguous(), smooth=True)
+    v8, v8s = qfa.quantize_v8(v[:, :, :L].contiguous())
+    O2, l2, _ = qfa.fwd_decode(None, None, k4, k4s, v8, v8s, L, 1 / math.sqrt(D), num_splits=3, kbar=kb, q_bf16=q)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)
