@@ -35,6 +35,13 @@ _lib = None
 TILE = 128
 BLOCK = 32
 
+# How P is quantised (tile_p in qfa_oracle.c)
+P_EXACT, P_E4M3, P_E4M3_BLOCK, P_E2M1_BLOCK = 0, 1, 2, 3
+# P/V formats of the whole path: the method (QK4PV8, one P scale per row), FP8 P
+# with one E8M0 scale per (row, 32 keys), and MXFP4 P and V ("QK4PV4").
+PV_FP8, PV_FP8_BLOCKP, PV_FP4 = 0, 1, 2
+_P_MODE_OF_PV = {PV_FP8: P_E4M3, PV_FP8_BLOCKP: P_E4M3_BLOCK, PV_FP4: P_E2M1_BLOCK}
+
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (plain C11, OpenMP)."""
@@ -80,6 +87,10 @@ def lib():
         L.orc_dequant_qk4.argtypes = [P, P, I64, I64, P]
         L.orc_dequant_v8.restype = None
         L.orc_dequant_v8.argtypes = [P, P, I64, I64, P]
+        L.orc_quantize_v4.restype = None
+        L.orc_quantize_v4.argtypes = [P, I64, I64, I64, I64, P, P]
+        L.orc_dequant_v4.restype = None
+        L.orc_dequant_v4.argtypes = [P, P, I64, I64, P]
         L.orc_attn_exact_rows.restype = None
         L.orc_attn_exact_rows.argtypes = [P, P, I64, P, P, I64, I64, I64, I, D, P, P]
         L.orc_attn_quant_rows.restype = None
@@ -199,6 +210,36 @@ def quantize_v8(v_bits: np.ndarray):
     return codes, scales
 
 
+def quantize_v4(v_bits: np.ndarray):
+    """v [B,H,S,D] bf16 bits -> MXFP4 (codes [B,H,ceil(S/32),D,16] u8, scales [B,H,ceil(S/32),D] u8)."""
+    v = _c(v_bits, np.uint16)
+    B, H, S, D = v.shape
+    nb = (S + BLOCK - 1) // BLOCK
+    codes = np.empty((B, H, nb, D, BLOCK // 2), np.uint8)
+    scales = np.empty((B, H, nb, D), np.uint8)
+    lib().orc_quantize_v4(_p(v), B, H, S, D, _p(codes), _p(scales))
+    return codes, scales
+
+
+def dequant_v4(codes: np.ndarray, scales: np.ndarray, S: int) -> np.ndarray:
+    """One (b, h) slice: codes [nb,D,16], scales [nb,D] -> [S,D]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    D = codes.shape[-2]
+    out = np.empty((S, D), np.float64)
+    lib().orc_dequant_v4(_p(codes), _p(scales), S, D, _p(out))
+    return out
+
+
+def _quant_dequant_v(vq: np.ndarray, L: int, pv: int) -> np.ndarray:
+    """V of one (b, kv head) [1,1,L,D] -> decoded [L,D] in the format of pv."""
+    if pv == PV_FP4:
+        vc, vs = quantize_v4(vq)
+        return dequant_v4(vc[0, 0], vs[0, 0], L)
+    vc, vs = quantize_v8(vq)
+    return dequant_v8(vc[0, 0], vs[0, 0], L)
+
+
 def dequant_qk4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     codes = _c(codes, np.uint8)
     scales = _c(scales, np.uint8)
@@ -236,10 +277,14 @@ def attn_exact_rows(Q, qpos, K, V, Sq, causal, softmax_scale):
 
 
 def attn_quant_rows(Q, qpos, K, V, Sq, causal, softmax_scale, Qc=None, Kbar=None, split_tiles=0,
-                    quantize_p=True, fp32_arg=True):
+                    quantize_p=True, fp32_arg=True, p_mode=None):
     """(c) the method's online-softmax schedule for rows Q [n,D] of one kv head.
     Q holds pre-scaled query rows q' = c2 q (see exp2_scale), so Q K^T is in
-    log2 units; softmax_scale still enters the compensation term."""
+    log2 units; softmax_scale still enters the compensation term.  p_mode
+    (P_EXACT .. P_E2M1_BLOCK) overrides quantize_p (True: P_E4M3, False:
+    P_EXACT)."""
+    if p_mode is None:
+        p_mode = P_E4M3 if quantize_p else P_EXACT
     Q = _c(Q, np.float64)
     K = _c(K, np.float64)
     V = _c(V, np.float64)
@@ -252,7 +297,7 @@ def attn_quant_rows(Q, qpos, K, V, Sq, causal, softmax_scale, Qc=None, Kbar=None
     lse = np.zeros(n, np.float64)
     lib().orc_attn_quant_rows(_p(Q), _p(Qc), _p(qpos), n, _p(K), _p(Kbar), _p(V), L, Sq, D,
                               int(bool(causal)), float(np.float32(softmax_scale)), int(split_tiles),
-                              int(bool(quantize_p)), int(bool(fp32_arg)), _p(O), _p(lse))
+                              int(p_mode), int(bool(fp32_arg)), _p(O), _p(lse))
     return O, lse
 
 
@@ -267,12 +312,13 @@ def _rows_by_group(rows: np.ndarray, Hq: int, Hkv: int):
 
 
 def prefill_rows(q_bits, k_bits, v_bits, rows: Sequence, causal: bool, softmax_scale: float,
-                 smooth: bool = False, exact: bool = True):
+                 smooth: bool = False, exact: bool = True, pv: int = PV_FP8):
     """Quantise Q/K/V with the oracle's quantizers and evaluate the listed rows.
 
     q_bits [B,Hq,Sq,D], k_bits/v_bits [B,Hkv,Skv,D] (bf16 bit patterns, uint16).
     rows: array [n,3] of (b, h, i).  Returns dict with O_q, lse_q (method) and,
-    if exact, O_x, lse_x (exact FP64 attention on the bf16 inputs).
+    if exact, O_x, lse_x (exact FP64 attention on the bf16 inputs).  pv picks
+    the P/V format: PV_FP8 (the method), PV_FP8_BLOCKP or PV_FP4.
     """
     rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
     B, Hq, Sq, D = q_bits.shape
@@ -289,9 +335,8 @@ def prefill_rows(q_bits, k_bits, v_bits, rows: Sequence, causal: bool, softmax_s
         kq = np.ascontiguousarray(k_bits[b:b + 1, g:g + 1])
         vq = np.ascontiguousarray(v_bits[b:b + 1, g:g + 1])
         kc, ks, kb = quantize_qk4(kq, smooth=smooth)
-        vc, vs = quantize_v8(vq)
         Kd = dequant_qk4(kc, ks)[0, 0]
-        Vd = dequant_v8(vc[0, 0], vs[0, 0], Skv)
+        Vd = _quant_dequant_v(vq, Skv, pv)
         Kbar = bf16_to_f64(kb[0, 0]) if smooth else None
         # query rows: quantise each needed (b, h) head once
         Qd = np.zeros((len(idx), D))
@@ -304,7 +349,7 @@ def prefill_rows(q_bits, k_bits, v_bits, rows: Sequence, causal: bool, softmax_s
             Qd[sel] = qd[r[sel, 2]]
             Qc[sel] = bf16_to_f64(q_bits[b, h][r[sel, 2]])
         O, lse = attn_quant_rows(Qd, r[:, 2], Kd, Vd, Sq, causal, softmax_scale,
-                                 Qc=Qc if smooth else None, Kbar=Kbar)
+                                 Qc=Qc if smooth else None, Kbar=Kbar, p_mode=_P_MODE_OF_PV[pv])
         out["O_q"][idx] = O
         out["lse_q"][idx] = lse
         if exact:
@@ -317,7 +362,7 @@ def prefill_rows(q_bits, k_bits, v_bits, rows: Sequence, causal: bool, softmax_s
 
 
 def decode_rows(q_bits, k_bits, v_bits, rows: Sequence, softmax_scale: float, num_splits: int,
-                kv_lens: Optional[Sequence[int]] = None, exact: bool = True):
+                kv_lens: Optional[Sequence[int]] = None, exact: bool = True, pv: int = PV_FP8):
     """Decode (one query token per sequence) with the split-KV schedule.
 
     q_bits [B,Hq,1,D]; k_bits/v_bits [B,Hkv,Smax,D].  rows [n,3] of (b, h, 0).
@@ -341,16 +386,15 @@ def decode_rows(q_bits, k_bits, v_bits, rows: Sequence, softmax_scale: float, nu
         kq = np.ascontiguousarray(k_bits[b:b + 1, g:g + 1, :L])
         vq = np.ascontiguousarray(v_bits[b:b + 1, g:g + 1, :L])
         kc, ks, _ = quantize_qk4(kq)
-        vc, vs = quantize_v8(vq)
         Kd = dequant_qk4(kc, ks)[0, 0]
-        Vd = dequant_v8(vc[0, 0], vs[0, 0], L)
+        Vd = _quant_dequant_v(vq, L, pv)
         Qd = np.zeros((len(idx), D))
         for j, (bb, h, _) in enumerate(r):
             qc_, qs_, _ = quantize_qk4(np.ascontiguousarray(q_bits[bb:bb + 1, h:h + 1]),
                                        prescale=exp2_scale(softmax_scale))
             Qd[j] = dequant_qk4(qc_, qs_)[0, 0, 0]
         O, lse = attn_quant_rows(Qd, np.zeros(len(idx), np.int64), Kd, Vd, 1, False, softmax_scale,
-                                 split_tiles=per)
+                                 split_tiles=per, p_mode=_P_MODE_OF_PV[pv])
         out["O_q"][idx] = O
         out["lse_q"][idx] = lse
         if exact:

@@ -65,6 +65,11 @@
  *    y = fl32(fl32(S) + fl32(c2 * fl32(delta))), m' = max(m, ceil(max y)),
  *    P = E4M3(256 * 2^(y - m')).  Without the compensation y = S exactly.
  *    Every exponential, sum and product is still evaluated in binary64.
+ *  - Contrast cases (not the method; see tile_p): P in E4M3 with one E8M0
+ *    scale per (row, 32 keys) instead of one per row, and MXFP4 P and V
+ *    ("QK4PV4": E2M1 codes, one E8M0 scale per 32 keys of a row for P and per
+ *    32 tokens of a channel for V).  A block's scale exponent is the ceiling of
+ *    its max, floored at 64 below the row's running max.
  */
 #include <math.h>
 #include <stdint.h>
@@ -301,6 +306,32 @@ void orc_quantize_v8(const uint16_t* v, int64_t B, int64_t H, int64_t S, int64_t
   }
 }
 
+/* V [B][H][S][D] bf16 -> MXFP4 codes [B][H][ceil(S/32)][D][16] and E8M0
+ * scales [B][H][ceil(S/32)][D]: the MXFP4 rule of the Q/K quantiser (e =
+ * ceil(log2 amax) - 2) applied to each block of 32 consecutive tokens of one
+ * channel, token 2k in the low nibble of byte k.  Tokens past S in the last
+ * block count as 0 (no effect on amax, code 0).  This is the V side of the
+ * full-FP4 "QK4PV4" contrast case ([MpFA] abstract; [FA4tut] "Direct-P": P
+ * and V in MXFP4 with one E8M0 scale per 32). */
+void orc_quantize_v4(const uint16_t* v, int64_t B, int64_t H, int64_t S, int64_t D,
+                     uint8_t* codes, uint8_t* scales) {
+  int64_t nblk = (S + QFA_ORC_BLOCK - 1) / QFA_ORC_BLOCK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    const uint16_t* vs = v + bh * S * D;
+    double buf[QFA_ORC_BLOCK];
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+      int64_t j0 = blk * QFA_ORC_BLOCK;
+      int64_t n = S - j0 < QFA_ORC_BLOCK ? S - j0 : QFA_ORC_BLOCK;
+      for (int64_t c = 0; c < D; ++c) {
+        for (int64_t t = 0; t < QFA_ORC_BLOCK; ++t) buf[t] = t < n ? orc_bf16_value(vs[(j0 + t) * D + c]) : 0.0;
+        scales[(bh * nblk + blk) * D + c] =
+            (uint8_t)mxfp4_block(buf, codes + ((bh * nblk + blk) * D + c) * (QFA_ORC_BLOCK / 2));
+      }
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------- */
 /* Dequantizers (exact in binary64)                                          */
 /* ------------------------------------------------------------------------- */
@@ -324,6 +355,18 @@ void orc_dequant_v8(const uint8_t* codes, const uint8_t* scales, int64_t S, int6
       int64_t blk = j / QFA_ORC_BLOCK;
       out[j * D + c] = orc_e4m3_value(codes[(blk * D + c) * QFA_ORC_BLOCK + j % QFA_ORC_BLOCK]) *
                        orc_e8m0_value(scales[blk * D + c]);
+    }
+}
+
+/* One (b, h) slice: codes [ceil(S/32)][D][16], scales [ceil(S/32)][D] -> [S][D]. */
+void orc_dequant_v4(const uint8_t* codes, const uint8_t* scales, int64_t S, int64_t D, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < S; ++j)
+    for (int64_t c = 0; c < D; ++c) {
+      int64_t blk = j / QFA_ORC_BLOCK, t = j % QFA_ORC_BLOCK;
+      uint8_t byte = codes[(blk * D + c) * (QFA_ORC_BLOCK / 2) + t / 2];
+      int code = (t & 1) ? (byte >> 4) : (byte & 15);
+      out[j * D + c] = orc_e2m1_value(code) * orc_e8m0_value(scales[blk * D + c]);
     }
 }
 
@@ -377,13 +420,71 @@ void orc_attn_exact_rows(const double* Q, const int64_t* qpos, int64_t n, const 
 
 #define LOG2E_F32 1.44269502162933349609375f /* binary32 nearest to log2(e) */
 
+/* P of one tile from the exponent arguments y[0..n) (masked keys -inf) and
+ * the row's new running max mnew, written as the values that multiply V and
+ * enter the denominator, in the frame of mnew:
+ *   QFA_P_EXACT        256 * 2^(y - mnew), not rounded (identity quantiser)
+ *   QFA_P_E4M3         E4M3(256 * 2^(y - mnew)): the method (QK4PV8), one
+ *                      power-of-two P scale per row
+ *   QFA_P_E4M3_BLOCK   per 32-key block b of the tile (keys 32b .. 32b+31
+ *                      from the tile start), e_b = max(ceil(max_{j in b} y_j),
+ *                      mnew - 64) and 2^(e_b - mnew) * E4M3(256 * 2^(y - e_b)):
+ *                      a dynamic E8M0 P scale per (row, 32 keys)
+ *   QFA_P_E2M1_BLOCK   the same blocks with 2^(e_b - mnew) * E2M1(4 * 2^(y - e_b)):
+ *                      MXFP4 P (the full-FP4 "QK4PV4" contrast case).  For
+ *                      a block whose max is the row's, e_b - 2 is the MX
+ *                      rule's ceil(log2 amax) - 2 with amax = 2^(max y - mnew).
+ * The floor mnew - 64 bounds how far below the row a block's scale may go
+ * (a block that far down holds no weight at binary32 precision); a block
+ * with no visible key gets it too and contributes 0.  The scale per (row, 32
+ * keys) follows [FA4tut] "Direct-P" (one E8M0 power-of-two scale per 32
+ * probabilities) and [MpFA] abstract (QK4PV8 vs fully FP4 attention). */
+#define QFA_P_EXACT 0
+#define QFA_P_E4M3 1
+#define QFA_P_E4M3_BLOCK 2
+#define QFA_P_E2M1_BLOCK 3
+#define QFA_P_BLOCK_FLOOR 64.0
+static void tile_p(const double* y, int64_t n, double mnew, int p_mode, double* P) {
+  if (p_mode == QFA_P_EXACT || p_mode == QFA_P_E4M3) {
+    for (int64_t j = 0; j < n; ++j) {
+      if (y[j] == -INFINITY) {
+        P[j] = 0.0;
+        continue;
+      }
+      double p = ldexp(exp2(y[j] - mnew), 8);
+      P[j] = p_mode == QFA_P_E4M3 ? orc_e4m3_value(orc_e4m3_encode(p)) : p;
+    }
+    return;
+  }
+  for (int64_t b0 = 0; b0 < n; b0 += QFA_ORC_BLOCK) {
+    int64_t b1 = b0 + QFA_ORC_BLOCK < n ? b0 + QFA_ORC_BLOCK : n;
+    double mu = -INFINITY;
+    for (int64_t j = b0; j < b1; ++j)
+      if (y[j] > mu) mu = y[j];
+    double e = ceil(mu);
+    if (!(e >= mnew - QFA_P_BLOCK_FLOOR)) e = mnew - QFA_P_BLOCK_FLOOR; /* also for mu = -inf */
+    for (int64_t j = b0; j < b1; ++j) {
+      if (y[j] == -INFINITY) {
+        P[j] = 0.0;
+        continue;
+      }
+      double v;
+      if (p_mode == QFA_P_E4M3_BLOCK)
+        v = orc_e4m3_value(orc_e4m3_encode(ldexp(exp2(y[j] - e), 8)));
+      else
+        v = orc_e2m1_value(orc_e2m1_encode(ldexp(exp2(y[j] - e), 2)));
+      P[j] = ldexp(v, (int)(e - mnew));
+    }
+  }
+}
+
 /* One split [t0, t1) of 128-token tiles for one query row.  q is the
  * pre-scaled query row (q' = c2 q, so q' . k is in log2 units).  Returns 0 if
  * no key of the split is visible (the split then has weight 0), else fills o
  * (already divided by l) and *lse_out. */
 static int split_row(const double* q, const double* qc, int64_t i, const double* K, const double* Kbar,
                      const double* V, int64_t L, int64_t Sq, int64_t D, int causal, float scale32,
-                     int64_t t0, int64_t t1, int quantize_p, int fp32_arg, double* o, double* lse_out,
+                     int64_t t0, int64_t t1, int p_mode, int fp32_arg, double* o, double* lse_out,
                      double* S, double* P) {
   const float c2f = scale32 * LOG2E_F32;          /* binary32 product, as the kernel */
   const double c2d = (double)scale32 * M_LOG2E;   /* binary64 */
@@ -411,43 +512,30 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
     double delta = 0.0;
     if (Kbar)
       for (int64_t c = 0; c < D; ++c) delta += qc[c] * Kbar[t * D + c];
-    double mnew, alpha;
+    /* exponent argument y_j of P (from here S holds y; masked keys stay -inf)
+     * and the new running max m' = max(m, ceil(max_j y_j)) */
+    double ymax = -INFINITY;
     if (fp32_arg) {
-      /* Exponent argument in binary32, as the kernel forms it:
-       *   y_j = fl32(fl32(S_j) + delta32),  delta32 = fl32(c2 * fl32(delta)),
-       *   m' = max(m, ceil(max_j y_j)),  P_j = E4M3(256 * 2^(y_j - m')). */
+      /* in binary32, as the kernel forms it:
+       *   y_j = fl32(fl32(S_j) + delta32),  delta32 = fl32(c2 * fl32(delta)) */
       const float d32 = Kbar ? c2f * (float)delta : 0.0f;
-      float ymax = -INFINITY;
       for (int64_t j = 0; j < j1 - j0; ++j) {
         if (S[j] == -INFINITY) continue;
         float y = (float)S[j] + d32;
-        S[j] = (double)y; /* from here S holds y */
-        if (y > ymax) ymax = y;
-      }
-      const double mt = ceil((double)ymax);
-      mnew = (m == -INFINITY || mt > m) ? mt : m;
-      alpha = (m == -INFINITY) ? 0.0 : exp2(m - mnew);
-      for (int64_t j = 0; j < j1 - j0; ++j) {
-        if (S[j] == -INFINITY) {
-          P[j] = 0.0;
-          continue;
-        }
-        double p = ldexp(exp2(S[j] - mnew), 8);
-        P[j] = quantize_p ? orc_e4m3_value(orc_e4m3_encode(p)) : p;
+        S[j] = (double)y;
+        if (S[j] > ymax) ymax = S[j];
       }
     } else {
-      double mt = ceil(smax + c2d * delta);
-      mnew = (mt > m) ? mt : m;
-      alpha = (m == -INFINITY) ? 0.0 : exp2(m - mnew);
       for (int64_t j = 0; j < j1 - j0; ++j) {
-        if (S[j] == -INFINITY) {
-          P[j] = 0.0;
-          continue;
-        }
-        double p = ldexp(exp2(S[j] + c2d * delta - mnew), 8);
-        P[j] = quantize_p ? orc_e4m3_value(orc_e4m3_encode(p)) : p;
+        if (S[j] == -INFINITY) continue;
+        S[j] += c2d * delta;
+        if (S[j] > ymax) ymax = S[j];
       }
     }
+    const double mt = ceil(ymax);
+    const double mnew = (m == -INFINITY || mt > m) ? mt : m;
+    const double alpha = (m == -INFINITY) ? 0.0 : exp2(m - mnew);
+    tile_p(S, j1 - j0, mnew, p_mode, P);
     /* running sum of the same (decoded) P values that multiply V, and output
      * rescale  [FA4tut "Direct-P"; "注意力慢在哪儿"] */
     double lt = 0.0;
@@ -463,7 +551,7 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
   }
   if (!any) return 0;
   for (int64_t c = 0; c < D; ++c) o[c] /= l;
-  *lse_out = M_LN2 * (m + log2(l / 256.0));
+  *lse_out = M_LN2 * (m + log2(l / (p_mode == QFA_P_E2M1_BLOCK ? 4.0 : 256.0)));
   return 1;
 }
 
@@ -476,14 +564,16 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
  *   qpos[n]     query index i in [0, Sq)
  *   K, V [L][D] keys and values (decoded), Kbar [ceil(L/128)][D] or NULL
  *   split_tiles 0: one split over all tiles; else tiles per decode split
- *   quantize_p  1: P rounded to E4M3; 0: identity quantiser (exact P)
+ *   p_mode      how P is quantised: QFA_P_EXACT (0, identity), QFA_P_E4M3
+ *               (1, the method), QFA_P_E4M3_BLOCK (2), QFA_P_E2M1_BLOCK (3);
+ *               see tile_p
  *   fp32_arg    1: exponent argument formed in binary32 (see split_row);
  *               0: everything in binary64
  * Outputs O [n][D], lse [n].  Rows with no visible key get O = 0, lse = -inf.
  */
 void orc_attn_quant_rows(const double* Q, const double* Qc, const int64_t* qpos, int64_t n, const double* K,
                          const double* Kbar, const double* V, int64_t L, int64_t Sq, int64_t D, int causal,
-                         float softmax_scale, int64_t split_tiles, int quantize_p, int fp32_arg, double* O,
+                         float softmax_scale, int64_t split_tiles, int p_mode, int fp32_arg, double* O,
                          double* lse) {
   int64_t nt = (L + QFA_ORC_TILE - 1) / QFA_ORC_TILE;
   int64_t per = split_tiles > 0 ? split_tiles : (nt > 0 ? nt : 1);
@@ -505,7 +595,7 @@ void orc_attn_quant_rows(const double* Q, const double* Qc, const int64_t* qpos,
       for (int64_t sp = 0; sp < nsplit; ++sp) {
         int64_t t0 = sp * per, t1 = t0 + per < nt ? t0 + per : nt;
         ok[sp] = split_row(Q + r * D, Qc ? Qc + r * D : NULL, qpos[r], K, Kbar, V, L, Sq, D, causal,
-                           softmax_scale, t0, t1, quantize_p, fp32_arg, os, &lses[sp], S, P);
+                           softmax_scale, t0, t1, p_mode, fp32_arg, os, &lses[sp], S, P);
         if (ok[sp]) {
           memcpy(outs + sp * D, os, sizeof(double) * D);
           if (lses[sp] > big) big = lses[sp];

@@ -309,3 +309,169 @@ def test_fp32_argument_with_compensation_close_to_fp64():
                                         split_tiles=per)
         assert np.abs(Os - O1).max() < 1e-4
         assert np.abs(ls - l1).max() < 1e-4
+
+
+# ----------------------------------------------------------------------------- P/V format variants
+def _two_block_case(y_b, vA, vB, L=64, D=4):
+    """One query row against 64 keys in two 32-key blocks: logit (log2 units)
+    0 in block A, y_b in block B; V rows vA in A and vB in B.  Q and K are
+    passed decoded, so the logits are exact."""
+    Q = np.zeros((1, D))
+    Q[0, 0] = 1.0
+    K = np.zeros((L, D))
+    K[32:, 0] = y_b
+    V = np.zeros((L, D))
+    V[:32] = vA
+    V[32:] = vB
+    return Q, K, V
+
+
+@pytest.mark.parametrize("p_mode", [oracle.P_E4M3, oracle.P_E4M3_BLOCK, oracle.P_E2M1_BLOCK])
+def test_block_p_scale_closed_form(p_mode):
+    """Block A at logit 0 and block B at logit -20.  With one P scale per row
+    (the method) block B's code 256 * 2^-20 = 2^-12 rounds to E4M3 zero, so
+    O = vA.  With a scale per (row, 32 keys) block B is coded against its own
+    max (code 256 or E2M1 4, exact) and weighted 2^-20, so
+    O = (vA + 2^-20 vB) / (1 + 2^-20) and LSE = ln(32 (1 + 2^-20))."""
+    vA = np.array([1.0, 0.5, -2.0, 0.0])
+    vB = np.array([3.0, -2.0, 6.0, 1.0])
+    Q, K, V = _two_block_case(-20.0, vA, vB)
+    O, lse = oracle.attn_quant_rows(Q, np.zeros(1, np.int64), K, V, 1, False, 0.125, p_mode=p_mode)
+    if p_mode == oracle.P_E4M3:
+        assert np.array_equal(O[0], vA)
+        assert abs(lse[0] - math.log(32.0)) < 1e-15
+    else:
+        w = 2.0**-20
+        assert np.abs(O[0] - (vA + w * vB) / (1 + w)).max() < 1e-15
+        assert abs(lse[0] - math.log(32.0 * (1 + w))) < 1e-14
+
+
+def test_block_p_scale_floor():
+    """A block more than 64 binades below the row is coded against m - 64:
+    at logit -70 its MXFP4 code is E2M1(4 * 2^-6) = 0 (smallest non-zero 1/2),
+    so it contributes nothing; its E4M3 code 256 * 2^-6 = 4 is exact, so there
+    it still contributes 2^-70 of its weight."""
+    vA = np.array([0.0, 1.0, 0.0, 0.0])
+    vB = np.array([5.0, 1.0, 0.0, 0.0])
+    Q, K, V = _two_block_case(-70.0, vA, vB)
+    O4, _ = oracle.attn_quant_rows(Q, np.zeros(1, np.int64), K, V, 1, False, 0.125, p_mode=oracle.P_E2M1_BLOCK)
+    assert O4[0, 0] == 0.0
+    O8, _ = oracle.attn_quant_rows(Q, np.zeros(1, np.int64), K, V, 1, False, 0.125, p_mode=oracle.P_E4M3_BLOCK)
+    w = 2.0**-70
+    assert O8[0, 0] == 5.0 * w / (1 + w)
+    # causal row 10 of 64 sees keys 0..10: block B has no visible key and
+    # contributes nothing; block A holds the row max, so the codes are the method's
+    Qr = np.tile(Q, (64, 1))
+    rng = np.random.default_rng(3)
+    Kr = K.copy()
+    Kr[:, 1] = rng.standard_normal(64)
+    Qr[:, 1] = 1.5
+    qpos = np.arange(64)
+    Ob, lb = oracle.attn_quant_rows(Qr, qpos, Kr, V, 64, True, 0.125, p_mode=oracle.P_E4M3_BLOCK)
+    Om, lm = oracle.attn_quant_rows(Qr, qpos, Kr, V, 64, True, 0.125, p_mode=oracle.P_E4M3)
+    assert np.array_equal(Ob[:32], Om[:32]) and np.array_equal(lb[:32], lm[:32])
+
+
+def _blockwise_bruteforce(s, Vd, p_mode):
+    """Brute force of the per-(row, 32 keys) P scale over 128-key tiles with
+    numpy exp2 and torch float8 (E4M3) or the printed E2M1 table (E2M1)."""
+    import json
+    import os
+    table = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "e2m1_magnitudes.json")))["magnitudes"]
+
+    def e2m1(a):
+        out = np.empty_like(a)
+        for idx, x in np.ndenumerate(a):
+            d = [abs(t - x) for t in table]
+            best = min(d)
+            c = [i for i, z in enumerate(d) if z == best]
+            if len(c) > 1:
+                c = [i for i in c if i % 2 == 0]
+            out[idx] = table[c[0]]
+        return out
+
+    n, L = s.shape
+    m = np.full((n, 1), -np.inf)
+    num = np.zeros((n, Vd.shape[1]))
+    den = np.zeros((n, 1))
+    for t0 in range(0, L, 128):
+        st = s[:, t0:t0 + 128]
+        mn = np.maximum(m, np.ceil(st.max(axis=1, keepdims=True)))
+        a = np.where(np.isneginf(m), 0.0, np.exp2(m - mn))
+        num *= a
+        den *= a
+        for b0 in range(0, st.shape[1], 32):
+            sb = st[:, b0:b0 + 32]
+            e = np.maximum(np.ceil(sb.max(axis=1, keepdims=True)), mn - 64)
+            if p_mode == oracle.P_E4M3_BLOCK:
+                p = _e4m3_torch(256.0 * np.exp2(sb - e))
+            else:
+                p = e2m1(4.0 * np.exp2(sb - e))
+            p = p * np.exp2(e - mn)
+            num += p @ Vd[t0 + b0:t0 + b0 + sb.shape[1]]
+            den += p.sum(axis=1, keepdims=True)
+        m = mn
+    return num / den
+
+
+@pytest.mark.parametrize("p_mode", [oracle.P_E4M3_BLOCK, oracle.P_E2M1_BLOCK])
+def test_block_p_scale_bruteforce(p_mode):
+    """Three tiles (the last one ragged) of random logits with a spread of
+    block maxima, recomputed by brute force."""
+    rng = np.random.default_rng(53)
+    Sq, L, D = 6, 300, 32
+    Qd, Kd, Vd = _quantized_inputs(rng, Sq, L, D, scale_q=3.0)
+    Kd[64:96] *= 0.25    # a block with small logits
+    Kd[200:232] -= 2.0   # and one shifted
+    scale = float(np.float32(0.125))
+    O, _ = oracle.attn_quant_rows(Qd, np.arange(Sq), Kd, Vd, Sq, False, scale, fp32_arg=False, p_mode=p_mode)
+    ref = _blockwise_bruteforce(Qd @ Kd.T, Vd, p_mode)
+    assert np.abs(O - ref).max() < 1e-12
+    # the row scale of the method gives a different result
+    O1, _ = oracle.attn_quant_rows(Qd, np.arange(Sq), Kd, Vd, Sq, False, scale, fp32_arg=False)
+    assert np.abs(O1 - O).max() > 1e-6
+
+
+def test_block_p_scale_equals_row_scale_when_every_block_reaches_the_max():
+    """If every 32-key block holds a key at the tile's max, every block's
+    exponent is the row's and the per-block E4M3 codes are the method's."""
+    rng = np.random.default_rng(59)
+    L, D = 256, 16
+    Q = np.zeros((3, D))
+    Q[:, 0] = 1.0
+    K = np.zeros((L, D))
+    K[:, 0] = -np.abs(rng.standard_normal(L)) * 3.0
+    K[::32, 0] = 0.5   # the tile max, once per block
+    V = rng.standard_normal((L, D))
+    O1, l1 = oracle.attn_quant_rows(Q, np.zeros(3, np.int64), K, V, 1, False, 0.125)
+    O2, l2 = oracle.attn_quant_rows(Q, np.zeros(3, np.int64), K, V, 1, False, 0.125, p_mode=oracle.P_E4M3_BLOCK)
+    assert np.array_equal(O1, O2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("pv", [oracle.PV_FP8_BLOCKP, oracle.PV_FP4])
+def test_pv_variants_close_to_exact_attention(pv):
+    """The variants run end to end through the drivers.  On N(0,1) data every
+    block's max lies within a few binades of its row's, so per-block FP8 P
+    scales give the method's codes exactly; MXFP4 P and V add error on top of
+    the method's (which MXFP4 Q and K dominate)."""
+    rng = np.random.default_rng(61)
+    B, Hq, Hkv, S, D = 1, 2, 1, 200, 64
+
+    def bf(x):
+        return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q = bf(rng.standard_normal((B, Hq, S, D)))
+    k = bf(rng.standard_normal((B, Hkv, S, D)))
+    v = bf(rng.standard_normal((B, Hkv, S, D)))
+    rows = np.array([(0, h, i) for h in range(Hq) for i in range(0, S, 7)])
+
+    def rel(r):
+        return np.linalg.norm(r["O_q"] - r["O_x"]) / np.linalg.norm(r["O_x"])
+    r0 = oracle.prefill_rows(q, k, v, rows, True, 0.125)
+    r1 = oracle.prefill_rows(q, k, v, rows, True, 0.125, pv=pv)
+    if pv == oracle.PV_FP8_BLOCKP:
+        assert np.array_equal(r1["O_q"], r0["O_q"])
+    else:
+        assert rel(r0) < rel(r1) < 2.5 * rel(r0)
+    d0 = oracle.decode_rows(q[:, :, :1], k, v, np.array([(0, 0, 0), (0, 1, 0)]), 0.125, 2)
+    d1 = oracle.decode_rows(q[:, :, :1], k, v, np.array([(0, 0, 0), (0, 1, 0)]), 0.125, 2, pv=pv)
+    assert rel(d1) < 2.5 * rel(d0) + 1e-12

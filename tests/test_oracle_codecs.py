@@ -272,3 +272,44 @@ def test_kbar_is_nearest_bf16_of_exact_mean():
     c2, s2, kb2 = oracle.quantize_qk4(b2, smooth=True)
     assert (kb2[0, 0, 0] == b2[0, 0, 0]).all()
     assert (s2 == 0).all() and ((c2 & 0x77) == 0).all()
+
+
+def test_v4_quantizer_bruteforce_vs_printed_table():
+    """MXFP4 V (the full-FP4 contrast case): each block of 32 consecutive
+    tokens of one channel gets e = ceil(log2 amax) - 2 and E2M1 codes by the
+    nearest-even rule over the printed magnitudes; token 2k in the low nibble
+    of byte k; tokens past S count as 0."""
+    table = gold("e2m1_magnitudes.json")["magnitudes"]
+    rng = np.random.default_rng(17)
+    B, H, S, D = 1, 2, 75, 32   # ragged: last block holds 11 tokens
+    v = rng.standard_normal((B, H, S, D)).astype(np.float32)
+    v[0, 1, 40, 7] = 50.0       # outlier
+    v[0, 0, 32:64, 3] = 0.0     # all-zero block
+    bits = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    codes, scales = oracle.quantize_v4(bits)
+    nb = (S + 31) // 32
+    assert codes.shape == (B, H, nb, D, 16) and scales.shape == (B, H, nb, D)
+    vv = oracle.bf16_to_f64(bits)
+    for h in range(H):
+        for blk in range(nb):
+            j0, j1 = blk * 32, min(S, blk * 32 + 32)
+            for c in range(D):
+                col = vv[0, h, j0:j1, c]
+                e = _block_scale_numpy(col, 2)
+                assert scales[0, h, blk, c] == e + 127
+                for t in range(32):
+                    a = col[t] * 2.0**-e if t < j1 - j0 else 0.0
+                    want = (8 if math.copysign(1.0, a) < 0 else 0) | _nearest_even_bruteforce(abs(a), table)
+                    byte = codes[0, h, blk, c, t // 2]
+                    got = (byte >> 4) if t % 2 else (byte & 15)
+                    assert got == want, (h, blk, c, t)
+        dq = oracle.dequant_v4(codes[0, h], scales[0, h], S)
+        assert dq.shape == (S, D)
+        # decoding the brute-forced codes by the printed table gives the same values
+        for j in (0, 17, 40, 74):
+            for c in (0, 3, 7):
+                blk = j // 32
+                byte = codes[0, h, blk, c, (j % 32) // 2]
+                code = (byte >> 4) if j % 2 else (byte & 15)
+                mag = table[code & 7] * 2.0 ** (int(scales[0, h, blk, c]) - 127)
+                assert dq[j, c] == (-mag if code & 8 else mag)
