@@ -26,9 +26,16 @@ QFA_ERR_UNSUPPORTED = 2
 QFA_ERR_WORKSPACE = 3
 QFA_ERR_HIP = 4
 
+# P/V formats (qfa_pv_format): the method, FP8 P with a scale per (row, 32
+# keys), MXFP4 P and V
+QFA_PV_FP8 = 0
+QFA_PV_FP8_BLOCKP = 1
+QFA_PV_FP4 = 2
+
 EXPORTS = (
     "qfa_quantize_qk4", "qfa_quantize_v8", "qfa_fwd_prefill", "qfa_fwd_decode",
     "qfa_decode_workspace_bytes", "qfa_decode_default_splits", "qfa_exp2_scale", "qfa_kv_append",
+    "qfa_fwd_prefill_ex", "qfa_fwd_decode_ex",
     "qfa_status_string", "qfa_version",
 )
 
@@ -58,6 +65,11 @@ def lib() -> ctypes.CDLL:
         L.qfa_fwd_decode.restype = I
         L.qfa_fwd_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P, I, F, I, ctypes.POINTER(I), P, SZ, P,
                                      P, P]
+        L.qfa_fwd_prefill_ex.restype = I
+        L.qfa_fwd_prefill_ex.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P]
+        L.qfa_fwd_decode_ex.restype = I
+        L.qfa_fwd_decode_ex.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P, I, F, I, I, ctypes.POINTER(I), P,
+                                        SZ, P, P, P]
         L.qfa_decode_workspace_bytes.restype = SZ
         L.qfa_decode_workspace_bytes.argtypes = [I, I, I, I]
         L.qfa_decode_default_splits.restype = I
@@ -148,6 +160,25 @@ def qfa_fwd_decode(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max
     return ns.value
 
 
+def qfa_fwd_prefill_ex(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_q, S_kv, D, causal, softmax_scale,
+                       block_size, pv_format, O, lse, stream=None):
+    _check("qfa_fwd_prefill_ex", lib().qfa_fwd_prefill_ex(
+        _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(None if kbar is None else _u16(kbar)),
+        _ptr(None if q_bf16 is None else _u16(q_bf16)), _ptr(v8), _ptr(v8s), B, Hq, Hkv, S_q, S_kv, D,
+        int(causal), float(softmax_scale), block_size, int(pv_format), _ptr(O), _ptr(lse), _stream(stream)))
+
+
+def qfa_fwd_decode_ex(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D, softmax_scale,
+                      block_size, pv_format, num_splits, workspace, workspace_bytes, O, lse, stream=None) -> int:
+    ns = ctypes.c_int(int(num_splits))
+    _check("qfa_fwd_decode_ex", lib().qfa_fwd_decode_ex(
+        _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(None if kbar is None else _u16(kbar)),
+        _ptr(None if q_bf16 is None else _u16(q_bf16)), _ptr(v8), _ptr(v8s), B, Hq, Hkv, S_kv_max,
+        _ptr(kv_lens), D, float(softmax_scale), block_size, int(pv_format), ctypes.byref(ns), _ptr(workspace),
+        int(workspace_bytes), _ptr(O), _ptr(lse), _stream(stream)))
+    return ns.value
+
+
 def qfa_kv_append(k_new, v_new, B, Hkv, n_new, D, S_kv_max, block_size, kv_lens, k4, k4s, kbar, v8, v8s, k_tail,
                   v_tail, stream=None):
     _check("qfa_kv_append", lib().qfa_kv_append(
@@ -200,8 +231,9 @@ def quantize_v8(v: torch.Tensor, stream=None):
 
 
 def fwd_prefill(q4, q4s, k4, k4s, v8, v8s, S_kv: int, causal: bool, softmax_scale: float, kbar=None,
-                q_bf16=None, with_lse: bool = True, stream=None):
-    """q4/q4s None: the kernel quantises q_bf16 [B,Hq,S_q,D] itself."""
+                q_bf16=None, with_lse: bool = True, pv_format: int = QFA_PV_FP8, stream=None):
+    """q4/q4s None: the kernel quantises q_bf16 [B,Hq,S_q,D] itself.  pv_format
+    picks the P/V format (v8/v8s then hold V in that format)."""
     if q4 is None:
         B, Hq, S_q, D = q_bf16.shape
     else:
@@ -210,13 +242,13 @@ def fwd_prefill(q4, q4s, k4, k4s, v8, v8s, S_kv: int, causal: bool, softmax_scal
     Hkv = k4.shape[1]
     O = torch.empty((B, Hq, S_q, D), dtype=torch.float32, device=k4.device)
     lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=k4.device) if with_lse else None
-    qfa_fwd_prefill(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_q, S_kv, D, causal, softmax_scale, 32,
-                    O, lse, stream)
+    qfa_fwd_prefill_ex(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_q, S_kv, D, causal, softmax_scale,
+                       32, pv_format, O, lse, stream)
     return O, lse
 
 
 def fwd_decode(q4, q4s, k4, k4s, v8, v8s, S_kv_max: int, softmax_scale: float, num_splits: int = 0,
-               kv_lens=None, kbar=None, q_bf16=None, workspace=None, stream=None):
+               kv_lens=None, kbar=None, q_bf16=None, workspace=None, pv_format: int = QFA_PV_FP8, stream=None):
     """q4 [B,Hq,1,D/2] (or None: the kernel quantises q_bf16 [B,Hq,1,D]);
     returns (O [B,Hq,D], lse [B,Hq], splits used)."""
     if q4 is None:
@@ -231,6 +263,6 @@ def fwd_decode(q4, q4s, k4, k4s, v8, v8s, S_kv_max: int, softmax_scale: float, n
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=k4.device)
     O = torch.empty((B, Hq, D), dtype=torch.float32, device=k4.device)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=k4.device)
-    used = qfa_fwd_decode(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D,
-                          softmax_scale, 32, splits, workspace, workspace.numel(), O, lse, stream)
+    used = qfa_fwd_decode_ex(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D,
+                             softmax_scale, 32, pv_format, splits, workspace, workspace.numel(), O, lse, stream)
     return O, lse, used

@@ -90,11 +90,27 @@ static qfa_status check_attn_common(const uint8_t* q4, const uint8_t* q4s, const
   return QFA_OK;
 }
 
+// QFA_PV_FP8 and QFA_PV_FP8_BLOCKP run; QFA_PV_FP4 is declared, not run.
+static qfa_status check_pv_format(int pv_format) {
+  if (pv_format == QFA_PV_FP8 || pv_format == QFA_PV_FP8_BLOCKP) return QFA_OK;
+  if (pv_format == QFA_PV_FP4) return QFA_ERR_UNSUPPORTED;
+  return QFA_ERR_INVALID_ARG;
+}
+
 qfa_status qfa_fwd_prefill(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
                            const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
                            int B, int Hq, int Hkv, int S_q, int S_kv, int D, int causal, float softmax_scale,
                            int block_size, float* O, float* lse, hipStream_t stream) {
+  return qfa_fwd_prefill_ex(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_q, S_kv, D, causal,
+                            softmax_scale, block_size, QFA_PV_FP8, O, lse, stream);
+}
+
+qfa_status qfa_fwd_prefill_ex(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                              const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                              int B, int Hq, int Hkv, int S_q, int S_kv, int D, int causal, float softmax_scale,
+                              int block_size, int pv_format, float* O, float* lse, hipStream_t stream) {
   if (S_q < 0 || S_kv < 0 || (causal != 0 && causal != 1)) return QFA_ERR_INVALID_ARG;
+  if (qfa_status f = check_pv_format(pv_format); f != QFA_OK) return f;
   if ((long long)B * Hq * S_q == 0) return QFA_OK;
   qfa_status st = check_attn_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, D, softmax_scale,
                                     block_size, O);
@@ -111,6 +127,7 @@ qfa_status qfa_fwd_prefill(const uint8_t* q4, const uint8_t* q4s, const uint8_t*
   a.causal = causal;
   a.c2 = softmax_scale * kLog2e;
   a.num_splits = 1;
+  a.pv = pv_format;
   return from_hip(qfa::launch_prefill(a, stream));
 }
 
@@ -155,7 +172,18 @@ qfa_status qfa_fwd_decode(const uint8_t* q4, const uint8_t* q4s, const uint8_t* 
                           int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens, int D,
                           float softmax_scale, int block_size, int* num_splits, void* workspace,
                           size_t workspace_bytes, float* O, float* lse, hipStream_t stream) {
+  return qfa_fwd_decode_ex(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D,
+                           softmax_scale, block_size, QFA_PV_FP8, num_splits, workspace, workspace_bytes, O, lse,
+                           stream);
+}
+
+qfa_status qfa_fwd_decode_ex(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                             const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                             int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens, int D,
+                             float softmax_scale, int block_size, int pv_format, int* num_splits, void* workspace,
+                             size_t workspace_bytes, float* O, float* lse, hipStream_t stream) {
   if (!num_splits || S_kv_max < 0 || *num_splits < 0 || *num_splits > 4096) return QFA_ERR_INVALID_ARG;
+  if (qfa_status f = check_pv_format(pv_format); f != QFA_OK) return f;
   qfa_status st = check_attn_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, D, softmax_scale,
                                     block_size, O);
   if (st != QFA_OK) return st;
@@ -181,6 +209,7 @@ qfa_status qfa_fwd_decode(const uint8_t* q4, const uint8_t* q4s, const uint8_t* 
   a.causal = 0;
   a.c2 = softmax_scale * kLog2e;
   a.num_splits = splits;
+  a.pv = pv_format;
   return from_hip(qfa::launch_decode(a, O, lse, stream));
 }
 

@@ -14,7 +14,7 @@ namespace qfa {
 
 // Decode: workgroup = one wave = (b, kv head g, row chunk rc, split s); lane row n
 // = query head g*G + 32*rc + n.  Writes normalised partials to the workspace.
-template <int D, bool COMP>
+template <int D, bool COMP, int PV>
 __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
   using TL = TileLayout<D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -74,9 +74,9 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
     uint8_t* buf = bufs + (t & 1) * TL::STRIDE;
     v16f s[4];
     v8i pb[2];
-    int pscale;
+    int pscale[2];
     qk_tile<D>(st, lo, buf, s);
-    softmax_tile<D, COMP>(st, s, t, kTile * t + kTile > L, L - 1, d32, pb, pscale);
+    softmax_tile<D, COMP, PV>(st, s, t, kTile * t + kTile > L, L - 1, d32, pb, pscale);
     pv_tile<D>(st, lo, buf + TL::V_OFF, pb, pscale);
     wait_vmem_all();
     if (t + 1 < t1) ld.fixup(t + 1, bufs + ((t + 1) & 1) * TL::STRIDE);
@@ -124,10 +124,15 @@ static hipError_t decode_d(const AttnArgs& a, float* O, float* lse, hipStream_t 
   if (nwg == 0) return hipSuccess;
   const bool comp = a.kbar != nullptr;
   const size_t lds = 2 * TL::STRIDE + (comp ? 32 * 32 * 4 : 0);
-  if (comp)
-    hipLaunchKernelGGL((k_decode_split<D, true>), dim3((unsigned)nwg), dim3(64), lds, s, a, nrc);
-  else
-    hipLaunchKernelGGL((k_decode_split<D, false>), dim3((unsigned)nwg), dim3(64), lds, s, a, nrc);
+#define QFA_SPLIT(C, PVF) hipLaunchKernelGGL((k_decode_split<D, C, PVF>), dim3((unsigned)nwg), dim3(64), lds, s, a, nrc)
+  if (a.pv == PV_FP8) {
+    if (comp) QFA_SPLIT(true, PV_FP8); else QFA_SPLIT(false, PV_FP8);
+  } else if (a.pv == PV_FP8_BLOCKP) {
+    if (comp) QFA_SPLIT(true, PV_FP8_BLOCKP); else QFA_SPLIT(false, PV_FP8_BLOCKP);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef QFA_SPLIT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = a.B * a.Hq;

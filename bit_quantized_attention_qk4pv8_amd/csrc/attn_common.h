@@ -269,17 +269,26 @@ struct RowState {
   v8i ones;        // FP8 1.0 in every byte: the A operand of the denominator product
 };
 
+// P/V formats.  PV_FP8 is the method: P = E4M3(256 * 2^(y - m)) with one
+// power-of-two scale per row (the running max m).  PV_FP8_BLOCKP gives P one
+// E8M0 scale per (row, 32 keys): block b is coded as E4M3(256 * 2^(y - e_b))
+// with e_b = max(ceil(max_{j in b} y_j), m - 64) and weighted 2^(e_b - m_ref)
+// through the MFMA's scale operand.  ([FA4tut] "Direct-P": one E8M0 scale per
+// 32 probabilities; [MpFA] abstract: FP8 P versus fully FP4 attention.)
+constexpr int PV_FP8 = 0, PV_FP8_BLOCKP = 1;
+
 // Softmax step of one tile.  s holds S' = Q'K^T, the logits in log2 units
 // (Q carries the factor softmax_scale * log2 e).  Masks keys > jlim (when
 // need_mask), adds the compensation offset d32 = fl32(c2 * delta) (COMP),
-// moves the running max m on the integer grid and converts
-// P = E4M3(256 * 2^(y - m)) into pb, the B operand of the P V product (pb[h]
-// covers keys 64h .. 64h+63).  pscale receives the E8M0 code of 2^(m - m_ref)
-// that the P V product applies.  O and l are touched only by the rare frame
-// rebase.
-template <int D, bool COMP>
+// moves the running max m on the integer grid and converts P (see PV_FP8)
+// into pb, the B operand of the P V product (pb[h] covers keys 64h .. 64h+63).
+// pscale[h] receives the E8M0 code that the P V product of half h applies:
+// 2^(m - m_ref) (PV_FP8), or 2^(e_b - m_ref) of the key block b = 2h + g
+// whose scale this lane supplies (PV_FP8_BLOCKP).  O and l are touched only
+// by the rare frame rebase.
+template <int D, bool COMP, int PV>
 __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int t, bool need_mask, int jlim,
-                                             float d32, v8i (&pb)[2], int& pscale) {
+                                             float d32, v8i (&pb)[2], int (&pscale)[2]) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   // ---- mask (diagonal / ragged tiles only); score s[c][rr] is key 128t + 32c + 16g + rr.
@@ -307,23 +316,47 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
 
   // ---- row max (two left-associated chains: max(max(m, a), b) compiles to
   // v_max3_f32, one instruction per two scores) and one lane swap
-  float mx0 = s[0][0], mx1 = s[2][0];
+  float mx;
+  float bmax[4];  // PV_FP8_BLOCKP: max of key block c (both lanes of the row)
+  if constexpr (PV == PV_FP8) {
+    float mx0 = s[0][0], mx1 = s[2][0];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int rr = (c == 0 ? 1 : 0); rr < 16; rr += 2) {
-      if (rr + 1 < 16) {
-        mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s[c][rr]), s[c][rr + 1]);
-        mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[c + 2][rr]), s[c + 2][rr + 1]);
-      } else {
-        mx0 = __builtin_fmaxf(mx0, s[c][rr]);
-        mx1 = __builtin_fmaxf(mx1, s[c + 2][rr]);
+      for (int rr = (c == 0 ? 1 : 0); rr < 16; rr += 2) {
+        if (rr + 1 < 16) {
+          mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s[c][rr]), s[c][rr + 1]);
+          mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[c + 2][rr]), s[c + 2][rr + 1]);
+        } else {
+          mx0 = __builtin_fmaxf(mx0, s[c][rr]);
+          mx1 = __builtin_fmaxf(mx1, s[c + 2][rr]);
+        }
       }
-    }
-  float mx = __builtin_fmaxf(mx0, mx1);
-  {
+    mx = __builtin_fmaxf(mx0, mx1);
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
     mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  } else {
+    // this lane's 16 keys of each block, then the partner lane's (l ^ 32)
+    // half: the first swap of (block 2h, block 2h+1) leaves in lane group g
+    // both halves of block 2h + g; the second hands each lane the other block
+    float pm[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float x = __builtin_fmaxf(s[c][0], s[c][1]);
+#pragma unroll
+      for (int rr = 2; rr < 16; rr += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, s[c][rr]), s[c][rr + 1]);
+      pm[c] = x;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[2 * h]), __float_as_uint(pm[2 * h + 1]), false,
+                                                 false);
+      const float f = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(f), __float_as_uint(f), false, false);
+      bmax[2 * h] = __uint_as_float(sw2[0]);
+      bmax[2 * h + 1] = __uint_as_float(sw2[1]);
+    }
+    mx = __builtin_fmaxf(__builtin_fmaxf(bmax[0], bmax[1]), __builtin_fmaxf(bmax[2], bmax[3]));
   }
   // Running max on the integer grid: every rescale factor is an exact power of
   // two, applied through the E8M0 scale of the P operand (no VALU work on O).
@@ -342,23 +375,43 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
     for (int rr = 0; rr < 16; ++rr) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(st.lv[rr]) : "v"(f));
     if (mn - st.m_ref > 64.0f) st.m_ref = mn;
   }
-  pscale = (mn == -__builtin_inff()) ? kScaleOne : kScaleOne + (int)(mn - st.m_ref);
-
-  // ---- P8 = E4M3(256 * 2^(y - m)), packed as the B operand of O^T += V^T P^T.
-  // The conversion divides by its scale operand, so 2^(m - 8) there turns
-  // 2^y into 256 * 2^(y - m) exactly, with no per-score subtraction.  That
-  // needs 2^y and the scale in binary32 range: while |m| <= 64 the keys that
-  // can give a non-zero code (y > m - 18) have 2^y in [2^-82, 2^64].  A wave
-  // with a row outside subtracts m from every score first.
-  const float e = (mn == -__builtin_inff()) ? 0.0f : mn;
-  const bool far = __builtin_amdgcn_ballot_w64(__builtin_fabsf(e) > 64.0f) != 0;
+  // ---- P8 = E4M3(256 * 2^(y - e)), packed as the B operand of O^T += V^T P^T,
+  // with e = m (PV_FP8) or e = e_c of the key block (PV_FP8_BLOCKP).  The
+  // conversion divides by its scale operand, so 2^(e - 8) there turns 2^y
+  // into 256 * 2^(y - e) exactly, with no per-score subtraction.  That needs
+  // 2^y and the scale in binary32 range: while e lies in [-100, 100] the keys
+  // that can give a non-zero code (y > e - 18) have 2^y in [2^-118, 2^100].
+  // A wave with an exponent outside subtracts it from the scores first.
+  float e[4];
+  if constexpr (PV == PV_FP8) {
+    pscale[0] = pscale[1] = (mn == -__builtin_inff()) ? kScaleOne : kScaleOne + (int)(mn - st.m_ref);
+    e[0] = e[1] = e[2] = e[3] = (mn == -__builtin_inff()) ? 0.0f : mn;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)  // also for a block with no visible key: the floor
+      e[c] = (mn == -__builtin_inff()) ? 0.0f : __builtin_fmaxf(__builtin_ceilf(bmax[c]), mn - 64.0f);
+    // lane group g supplies the scale of block 2h + g (a mask select: an
+    // indexed e[2h + g] would put e in scratch memory)
+    const int gm = -((threadIdx.x & 63) >> 5);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int d0 = (int)(e[2 * h] - st.m_ref), d1 = (int)(e[2 * h + 1] - st.m_ref);
+      pscale[h] = (mn == -__builtin_inff()) ? kScaleOne : kScaleOne + (d0 ^ ((d0 ^ d1) & gm));
+    }
+  }
+  bool out_of_range = false;
+#pragma unroll
+  for (int c = 0; c < (PV == PV_FP8 ? 1 : 4); ++c) out_of_range |= __builtin_fabsf(e[c]) > 100.0f;
+  const bool far = __builtin_amdgcn_ballot_w64(out_of_range) != 0;
   if (far) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) s[c][rr] -= e;
+      for (int rr = 0; rr < 16; ++rr) s[c][rr] -= e[c];
   }
-  const float cs = far ? 0x1p-8f : __builtin_ldexpf(1.0f, (int)e - 8);
+  float cs[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) cs[c] = far ? 0x1p-8f : __builtin_ldexpf(1.0f, (int)e[c] - 8);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -371,8 +424,8 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
       const float p3 = __builtin_amdgcn_exp2f(s[c][r0 + 3]);
       // the old value of the destination is dead (both halves are written): reuse p0's register
       v2s w = __builtin_bit_cast(v2s, p0);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p0, p1, cs, false);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p2, p3, cs, true);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p0, p1, cs[c], false);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p2, p3, cs[c], true);
       pb[h][k] = __builtin_bit_cast(int, w);
     }
 }
@@ -432,8 +485,8 @@ struct NoHook {
 // matrix unit is busy.
 template <int D, class Hook = NoHook>
 __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D>& lo, const uint8_t* vreg,
-                                           const v8i (&pb)[2], int pscale, const uint8_t* kreg, v16f (&s)[4],
-                                           const Hook& hook = Hook()) {
+                                           const v8i (&pb)[2], const int (&pscale)[2], const uint8_t* kreg,
+                                           v16f (&s)[4], const Hook& hook = Hook()) {
   constexpr int NQ = 2 * (D / 32);  // P V products (excluding the denominator)
   constexpr int R = 3;              // V operands in flight
   v8i va[R];
@@ -445,8 +498,8 @@ __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D>& l
   for (int q = 0; q < NQ; ++q) {
     __builtin_amdgcn_sched_barrier(0);
     const int h = q / (D / 32), cb = q % (D / 32);
-    st.o[cb] = mfma_fp8_32x32x64(va[q % R], pb[h], st.o[cb], vs[q % R], pscale);
-    if (cb == D / 32 - 1) st.lv = mfma_fp8_32x32x64(st.ones, pb[h], st.lv, kScaleOne, pscale);
+    st.o[cb] = mfma_fp8_32x32x64(va[q % R], pb[h], st.o[cb], vs[q % R], pscale[h]);
+    if (cb == D / 32 - 1) st.lv = mfma_fp8_32x32x64(st.ones, pb[h], st.lv, kScaleOne, pscale[h]);
     if (q + R < NQ)
       load_v_op<D>(vreg, lo, q + R, va[q % R], vs[q % R]);
     else if (q + R - NQ < 2)
@@ -466,7 +519,7 @@ __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D>& l
 // P V of one tile alone, pipelined like pv_then_qk.
 template <int D>
 __device__ __forceinline__ void pv_tile(RowState<D>& st, const LaneOffs<D>& lo, const uint8_t* vreg,
-                                        const v8i (&pb)[2], int pscale) {
+                                        const v8i (&pb)[2], const int (&pscale)[2]) {
   constexpr int NQ = 2 * (D / 32);
   constexpr int R = 3;
   v8i va[R];
@@ -477,8 +530,8 @@ __device__ __forceinline__ void pv_tile(RowState<D>& st, const LaneOffs<D>& lo, 
   for (int q = 0; q < NQ; ++q) {
     __builtin_amdgcn_sched_barrier(0);
     const int h = q / (D / 32), cb = q % (D / 32);
-    st.o[cb] = mfma_fp8_32x32x64(va[q % R], pb[h], st.o[cb], vs[q % R], pscale);
-    if (cb == D / 32 - 1) st.lv = mfma_fp8_32x32x64(st.ones, pb[h], st.lv, kScaleOne, pscale);
+    st.o[cb] = mfma_fp8_32x32x64(va[q % R], pb[h], st.o[cb], vs[q % R], pscale[h]);
+    if (cb == D / 32 - 1) st.lv = mfma_fp8_32x32x64(st.ones, pb[h], st.lv, kScaleOne, pscale[h]);
     if (q + R < NQ) load_v_op<D>(vreg, lo, q + R, va[q % R], vs[q % R]);
   }
   __builtin_amdgcn_sched_barrier(0);

@@ -80,7 +80,7 @@ __device__ __forceinline__ void window_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool COMP>
+template <int D, bool COMP, int PV>
 __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) {
   using TL = TileLayout<D>;
   constexpr int NB = kPrefillBuffers;  // LDS buffers per operand
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   __syncthreads();
 
   v8i pb[2];  // P of the last softmax, consumed by the next products
-  int pscale = kScaleOne;
+  int pscale[2] = {kScaleOne, kScaleOne};
   int kb_cur = 0, vb_prev = NB - 1;  // buffer of K(t) and of V(t-1)
 #pragma nounroll
   for (int t = 0; t <= T; ++t) {
@@ -226,7 +226,7 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
     if (t < Tw) {
       const float d32 = COMP ? a.c2 * dl[(t & 31) * 32 + n] : 0.0f;
       const bool need_mask = (kTile * t + kTile - 1 > jmin_w) || (kTile * t + kTile > L);
-      softmax_tile<D, COMP>(st, s, t, need_mask, jlim, d32, pb, pscale);
+      softmax_tile<D, COMP, PV>(st, s, t, need_mask, jlim, d32, pb, pscale);
     }
     if (half == 0) end_window();
     kb_cur = kb_cur + 1 == NB ? 0 : kb_cur + 1;
@@ -245,10 +245,15 @@ static hipError_t prefill_d(const AttnArgs& a, hipStream_t s) {
   if (nwg == 0) return hipSuccess;
   const bool comp = a.kbar != nullptr;
   const size_t lds = kPrefillBuffers * (TL::KREG + TL::VREG) + 1024 + (comp ? (size_t)8 * 32 * 32 * 4 : 0);
-  if (comp)
-    hipLaunchKernelGGL((k_prefill<D, true>), dim3((unsigned)nwg), dim3(512), lds, s, a, nwg_per_group);
-  else
-    hipLaunchKernelGGL((k_prefill<D, false>), dim3((unsigned)nwg), dim3(512), lds, s, a, nwg_per_group);
+#define QFA_PREFILL(C, PVF) hipLaunchKernelGGL((k_prefill<D, C, PVF>), dim3((unsigned)nwg), dim3(512), lds, s, a, nwg_per_group)
+  if (a.pv == PV_FP8) {
+    if (comp) QFA_PREFILL(true, PV_FP8); else QFA_PREFILL(false, PV_FP8);
+  } else if (a.pv == PV_FP8_BLOCKP) {
+    if (comp) QFA_PREFILL(true, PV_FP8_BLOCKP); else QFA_PREFILL(false, PV_FP8_BLOCKP);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef QFA_PREFILL
   return hipGetLastError();
 }
 

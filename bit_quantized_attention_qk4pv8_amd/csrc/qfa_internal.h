@@ -133,6 +133,7 @@ struct AttnArgs {
   int causal;
   float c2;               // softmax_scale * log2(e), rounded to binary32
   int num_splits;         // decode
+  int pv;                 // P/V format (PV_FP8, PV_FP8_BLOCKP)
 };
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);

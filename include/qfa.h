@@ -160,6 +160,38 @@ qfa_status qfa_fwd_decode(const uint8_t* q4, const uint8_t* q4s, const uint8_t* 
                           size_t workspace_bytes, float* O, float* lse, hipStream_t stream);
 
 /*
+ * P/V formats.  QFA_PV_FP8 is the method described above.  The other two are
+ * contrast cases: the MpFA abstract sets QK4PV8 against fully FP4 attention,
+ * and the FP4 tutorial's "Direct-P" section gives P one E8M0 power-of-two
+ * scale per 32 probabilities.
+ *   QFA_PV_FP8_BLOCKP  P in E4M3 with one E8M0 scale per (row, 32 keys): key
+ *                      block b (32 keys from a multiple of 32) of a tile is
+ *                      coded as E4M3(256 * 2^(y_j - e_b)) with
+ *                      e_b = max(ceil(max_{j in b} y_j), m' - 64), and those
+ *                      codes count 2^(e_b - m') in O and l.  V as for QFA_PV_FP8.
+ *   QFA_PV_FP4         P in MXFP4, E2M1(4 * 2^(y_j - e_b)) on the same blocks,
+ *                      and V in MXFP4 (qfa_quantize_v4); LSE = ln(l / 4) + m ln 2.
+ */
+typedef enum qfa_pv_format { QFA_PV_FP8 = 0, QFA_PV_FP8_BLOCKP = 1, QFA_PV_FP4 = 2 } qfa_pv_format;
+
+/*
+ * qfa_fwd_prefill and qfa_fwd_decode with the P/V format as an argument; the
+ * plain entry points are pv_format = QFA_PV_FP8.  For QFA_PV_FP4, v8 and v8s
+ * carry the MXFP4 V of qfa_quantize_v4.  An unknown format gives
+ * QFA_ERR_INVALID_ARG, a known one this library does not run
+ * QFA_ERR_UNSUPPORTED.  Everything else is as for the plain entry points.
+ */
+qfa_status qfa_fwd_prefill_ex(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                              const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                              int B, int Hq, int Hkv, int S_q, int S_kv, int D, int causal, float softmax_scale,
+                              int block_size, int pv_format, float* O, float* lse, hipStream_t stream);
+qfa_status qfa_fwd_decode_ex(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                             const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                             int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens, int D,
+                             float softmax_scale, int block_size, int pv_format, int* num_splits, void* workspace,
+                             size_t workspace_bytes, float* O, float* lse, hipStream_t stream);
+
+/*
  * KV-cache writer: append n_new tokens to every sequence of a pre-quantised
  * cache (quantise on write: hnwysp.cn MXAttention/MXFP4 notes, sections 3.4
  * and 5.4; the cache feeds qfa_fwd_decode).  Sequence b holds L_b tokens

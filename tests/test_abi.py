@@ -116,6 +116,31 @@ def test_validation_rejects_before_launch():
     assert st == qfa.QFA_ERR_INVALID_ARG
 
 
+def test_pv_format_validation():
+    """The _ex entry points take the P/V format: an unknown one is an invalid
+    argument (checked before anything else is read); every other check is the
+    plain entry point's."""
+    P = ctypes.c_void_p
+    F = ctypes.c_float
+    fake = P(4096)
+    pre = lambda fmt, Hkv=2: _call_raw(
+        "qfa_fwd_prefill_ex", fake, fake, fake, fake, None, None, fake, fake, 1, 4, Hkv, 8, 8, 128, 1, F(0.125), 32,
+        fmt, fake, None, None)
+    for bad in (-1, 3, 99):
+        assert pre(bad) == qfa.QFA_ERR_INVALID_ARG
+    assert pre(qfa.QFA_PV_FP8, Hkv=3) == qfa.QFA_ERR_INVALID_ARG       # Hq % Hkv, as for the plain call
+    assert pre(qfa.QFA_PV_FP8_BLOCKP, Hkv=3) == qfa.QFA_ERR_INVALID_ARG
+    ns = ctypes.c_int(4)
+    dec = lambda fmt, ws=16: _call_raw(
+        "qfa_fwd_decode_ex", fake, fake, fake, fake, None, None, fake, fake, 2, 8, 2, 1024, None, 128, F(0.1), 32,
+        fmt, ctypes.byref(ns), fake, ctypes.c_size_t(ws), fake, None, None)
+    assert dec(5) == qfa.QFA_ERR_INVALID_ARG
+    assert dec(qfa.QFA_PV_FP8_BLOCKP) == qfa.QFA_ERR_WORKSPACE          # workspace too small, as before
+    # the plain entry points are the method's format
+    assert _call_raw("qfa_fwd_prefill", fake, fake, fake, fake, None, None, fake, fake, 1, 4, 3, 8, 8, 128, 1,
+                     F(0.125), 32, fake, None, None) == qfa.QFA_ERR_INVALID_ARG
+
+
 def test_kv_append_validation():
     P = ctypes.c_void_p
     fake, odd = P(4096), P(4097)

@@ -32,8 +32,13 @@ def _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed, k_offset=0.0, q_scale=1.0):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
-def _gpu_prefill(q, k, v, causal, scale, smooth, fused=False):
-    """fused: Q goes in as bf16 and the prefill kernel quantises it (q4 = q4s = NULL)."""
+def _quantize_v(v, pv):
+    return qfa.quantize_v4(v) if pv == qfa.QFA_PV_FP4 else qfa.quantize_v8(v)
+
+
+def _gpu_prefill(q, k, v, causal, scale, smooth, fused=False, pv=qfa.QFA_PV_FP8):
+    """fused: Q goes in as bf16 and the prefill kernel quantises it (q4 = q4s = NULL).
+    pv: the P/V format."""
     B, Hq, Sq, D = q.shape
     Skv = k.shape[2]
     if fused:
@@ -41,19 +46,20 @@ def _gpu_prefill(q, k, v, causal, scale, smooth, fused=False):
     else:
         q4, q4s, _ = qfa.quantize_qk4(q, prescale=qfa.qfa_exp2_scale(scale))
     k4, k4s, kbar = qfa.quantize_qk4(k, smooth=smooth)
-    v8, v8s = qfa.quantize_v8(v)
+    v8, v8s = _quantize_v(v, pv)
     O, lse = qfa.fwd_prefill(q4, q4s, k4, k4s, v8, v8s, Skv, causal, scale, kbar=kbar,
-                             q_bf16=q if (smooth or fused) else None)
+                             q_bf16=q if (smooth or fused) else None, pv_format=pv)
     torch.cuda.synchronize()
     return O, lse
 
 
-def _check_prefill(q, k, v, causal, scale, smooth, rows, label, fused=False):
+def _check_prefill(q, k, v, causal, scale, smooth, rows, label, fused=False, pv=qfa.QFA_PV_FP8):
     B, Hq, Sq, D = q.shape
     say("prefill", label, "q", tuple(q.shape), "k", tuple(k.shape), "causal", causal, "smooth", smooth,
-        "fused Q" if fused else "")
-    O, lse = _gpu_prefill(q, k, v, causal, scale, smooth, fused)
-    res = oracle.prefill_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, causal, scale, smooth=smooth)
+        "fused Q" if fused else "", "pv", pv)
+    O, lse = _gpu_prefill(q, k, v, causal, scale, smooth, fused, pv)
+    res = oracle.prefill_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, causal, scale, smooth=smooth,
+                              pv=pv)
     Og = to_np(O)[rows[:, 0], rows[:, 1], rows[:, 2]]
     lg = to_np(lse)[rows[:, 0], rows[:, 1], rows[:, 2]]
     compare_o(Og, res["O_q"], lg, res["lse_q"], label)
@@ -150,7 +156,7 @@ def test_prefill_workload_sampled(name, nrows):
 
 
 # ----------------------------------------------------------------------------- decode
-def _gpu_decode(q, k, v, num_splits, kv_lens=None, smooth=False, fused=False):
+def _gpu_decode(q, k, v, num_splits, kv_lens=None, smooth=False, fused=False, pv=qfa.QFA_PV_FP8):
     B, Hq, _, D = q.shape
     Smax = k.shape[2]
     if fused:
@@ -158,34 +164,48 @@ def _gpu_decode(q, k, v, num_splits, kv_lens=None, smooth=False, fused=False):
     else:
         q4, q4s, _ = qfa.quantize_qk4(q, prescale=qfa.qfa_exp2_scale(1 / math.sqrt(D)))
     k4, k4s, kbar = qfa.quantize_qk4(k, smooth=smooth)
-    v8, v8s = qfa.quantize_v8(v)
+    v8, v8s = _quantize_v(v, pv)
+    if kv_lens is not None:
+        # a cache holds what the writer quantised: each sequence's own L_b tokens
+        # (its last K-mean tile and V block cover only those)
+        for b, L in enumerate(kv_lens):
+            if L == 0:
+                continue
+            kc, ksc, kb = qfa.quantize_qk4(k[b:b + 1, :, :L].contiguous(), smooth=smooth)
+            vc, vsc = _quantize_v(v[b:b + 1, :, :L].contiguous(), pv)
+            k4[b:b + 1, :, :L] = kc
+            k4s[b:b + 1, :, :L] = ksc
+            if smooth:
+                kbar[b:b + 1, :, :kb.shape[2]] = kb
+            v8[b:b + 1, :, :vc.shape[2]] = vc
+            v8s[b:b + 1, :, :vsc.shape[2]] = vsc
     lens = None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32, device="cuda")
     O, lse, used = qfa.fwd_decode(q4, q4s, k4, k4s, v8, v8s, Smax, 1 / math.sqrt(D), num_splits=num_splits,
-                                  kv_lens=lens, kbar=kbar, q_bf16=q if (smooth or fused) else None)
+                                  kv_lens=lens, kbar=kbar, q_bf16=q if (smooth or fused) else None, pv_format=pv)
     torch.cuda.synchronize()
     return O, lse, used
 
 
-def _check_decode(q, k, v, num_splits, kv_lens=None, label="", seqs=None, smooth=False):
+def _check_decode(q, k, v, num_splits, kv_lens=None, label="", seqs=None, smooth=False, pv=qfa.QFA_PV_FP8):
     B, Hq, _, D = q.shape
-    say("decode", label, "q", tuple(q.shape), "k", tuple(k.shape), "splits", num_splits)
-    O, lse, used = _gpu_decode(q, k, v, num_splits, kv_lens, smooth)
+    say("decode", label, "q", tuple(q.shape), "k", tuple(k.shape), "splits", num_splits, "pv", pv)
+    O, lse, used = _gpu_decode(q, k, v, num_splits, kv_lens, smooth, pv=pv)
     if num_splits:
         assert used == num_splits
     seqs = list(range(B)) if seqs is None else seqs
     rows = np.array([(b, h, 0) for b in seqs for h in range(Hq)], dtype=np.int64)
     if smooth:
-        res = _decode_oracle_smooth(q, k, v, rows, used, kv_lens)
+        res = _decode_oracle_smooth(q, k, v, rows, used, kv_lens, pv)
     else:
         res = oracle.decode_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, 1 / math.sqrt(D), used,
-                                 kv_lens=kv_lens)
+                                 kv_lens=kv_lens, pv=pv)
     Og = to_np(O)[rows[:, 0], rows[:, 1]]
     lg = to_np(lse)[rows[:, 0], rows[:, 1]]
     compare_o(Og, res["O_q"], lg, res["lse_q"], label)
     return used
 
 
-def _decode_oracle_smooth(q, k, v, rows, splits, kv_lens):
+def _decode_oracle_smooth(q, k, v, rows, splits, kv_lens, pv=oracle.PV_FP8):
     """Oracle decode with K smoothing: quantise with the oracle, run the split schedule."""
     qb, kb, vb = bf16_bits(q), bf16_bits(k), bf16_bits(v)
     B, Hq, _, D = qb.shape
@@ -198,13 +218,20 @@ def _decode_oracle_smooth(q, k, v, rows, splits, kv_lens):
         nt = (L + 127) // 128
         per = max(1, -(-nt // splits))
         kc, ks, kbar = oracle.quantize_qk4(np.ascontiguousarray(kb[b:b + 1, g:g + 1, :L]), smooth=True)
-        vc, vs = oracle.quantize_v8(np.ascontiguousarray(vb[b:b + 1, g:g + 1, :L]))
+        vsl = np.ascontiguousarray(vb[b:b + 1, g:g + 1, :L])
+        if pv == oracle.PV_FP4:
+            vc, vs = oracle.quantize_v4(vsl)
+            Vd = oracle.dequant_v4(vc[0, 0], vs[0, 0], L)
+        else:
+            vc, vs = oracle.quantize_v8(vsl)
+            Vd = oracle.dequant_v8(vc[0, 0], vs[0, 0], L)
         qc, qs, _ = oracle.quantize_qk4(np.ascontiguousarray(qb[b:b + 1, h:h + 1]),
                                         prescale=oracle.exp2_scale(1 / math.sqrt(D)))
         O, l = oracle.attn_quant_rows(oracle.dequant_qk4(qc, qs)[0, 0], np.zeros(1, np.int64),
-                                      oracle.dequant_qk4(kc, ks)[0, 0], oracle.dequant_v8(vc[0, 0], vs[0, 0], L),
+                                      oracle.dequant_qk4(kc, ks)[0, 0], Vd,
                                       1, False, 1 / math.sqrt(D), Qc=oracle.bf16_to_f64(qb[b, h]),
-                                      Kbar=oracle.bf16_to_f64(kbar[0, 0]), split_tiles=per)
+                                      Kbar=oracle.bf16_to_f64(kbar[0, 0]), split_tiles=per,
+                                      p_mode=oracle._P_MODE_OF_PV[pv])
         out["O_q"][n] = O[0]
         out["lse_q"][n] = l[0]
     return out
@@ -242,3 +269,71 @@ def test_decode_fused_q_matches_two_pass(smooth):
     O2, l2, u2 = _gpu_decode(q, k, v, 3, kv_lens=[1000, 517, 0], smooth=smooth, fused=True)
     assert u1 == u2 == 3
     assert torch.equal(O1, O2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------- P/V formats and extreme logits
+BLOCKP_CASES = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, smooth, k_offset, label
+    (1, 4, 1, 333, 333, 128, True, False, 0.0, "blockp-causal-ragged-G4"),
+    (2, 5, 1, 70, 700, 64, False, False, 0.0, "blockp-d64-G5"),
+    (1, 2, 1, 200, 600, 128, True, True, 3.0, "blockp-compensation"),
+]
+
+
+@pytest.mark.parametrize("case", BLOCKP_CASES, ids=[c[-1] for c in BLOCKP_CASES])
+def test_prefill_blockp_small_all_rows(case):
+    B, Hq, Hkv, Sq, Skv, D, causal, smooth, koff, label = case
+    q, k, v = _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed=zlib.crc32(label.encode()) % 1000, k_offset=koff, q_scale=2.0)
+    _check_prefill(q, k, v, causal, 1.0 / math.sqrt(D), smooth, _all_rows(B, Hq, Sq), label, fused=True,
+                   pv=qfa.QFA_PV_FP8_BLOCKP)
+
+
+def _spread_inputs(seed, Sq=128, Skv=1000, D=128):
+    """Strongly peaked rows whose 32-key blocks sit many binades apart: Q and
+    K scaled up, the keys of every other block scaled down."""
+    q, k, v = _rand_inputs(1, 2, 1, Sq, Skv, D, seed=seed, q_scale=4.0)
+    k = k.float()
+    k *= 2.0
+    blk = (torch.arange(Skv, device="cuda") // 32) % 2 == 1
+    k[:, :, blk] *= 0.15
+    return q, k.to(torch.bfloat16), v
+
+
+def test_prefill_blockp_differs_where_blocks_spread():
+    """Where block maxima lie far below the row's, per-block P scales keep
+    codes that one scale per row rounds to zero: the two formats then give
+    different O, each matching its own oracle."""
+    q, k, v = _spread_inputs(seed=5)
+    rows = _all_rows(1, 2, 128)
+    O1, _ = _check_prefill(q, k, v, False, 1.0 / math.sqrt(128), False, rows, "spread-blockp", fused=True,
+                           pv=qfa.QFA_PV_FP8_BLOCKP)
+    O0, _ = _check_prefill(q, k, v, False, 1.0 / math.sqrt(128), False, rows, "spread-fp8", fused=True)
+    d = (O1 - O0).abs().max().item()
+    say("spread: max |O_blockp - O_fp8| = %.3e" % d)
+    assert d > 0
+
+
+@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8, qfa.QFA_PV_FP8_BLOCKP])
+def test_prefill_extreme_logits_far_and_rebase(pv):
+    """Logits far beyond 100 in log2 units (the kernel's subtract-first path)
+    and a row max that climbs by more than 64 binades across the key range
+    (the frame rebase of O and l)."""
+    Skv, D = 1200, 128
+    q, k, v = _rand_inputs(1, 2, 1, 64, Skv, D, seed=9, q_scale=30.0)
+    k = (k.float() * (1.0 + torch.arange(Skv, device="cuda").float() / 200.0)[None, None, :, None]).to(torch.bfloat16)
+    _check_prefill(q, k, v, False, 1.0 / math.sqrt(D), False, _all_rows(1, 2, 64), "extreme-logits", fused=True,
+                   pv=pv)
+
+
+@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8, qfa.QFA_PV_FP8_BLOCKP])
+def test_decode_extreme_logits(pv):
+    Skv, D = 1200, 128
+    q, k, v = _rand_inputs(2, 8, 2, 1, Skv, D, seed=10, q_scale=30.0)
+    k = (k.float() * (1.0 + torch.arange(Skv, device="cuda").float() / 200.0)[None, None, :, None]).to(torch.bfloat16)
+    _check_decode(q, k, v, 3, kv_lens=[1200, 700], label="decode-extreme", pv=pv)
+
+
+@pytest.mark.parametrize("smooth", [False, True])
+def test_decode_blockp(smooth):
+    q, k, v = _rand_inputs(3, 8, 2, 1, 1000, 128, seed=23, q_scale=2.0, k_offset=3.0 if smooth else 0.0)
+    _check_decode(q, k, v, 3, kv_lens=[1000, 517, 0], label="decode-blockp", smooth=smooth, pv=qfa.QFA_PV_FP8_BLOCKP)
