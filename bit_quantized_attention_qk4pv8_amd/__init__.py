@@ -35,7 +35,7 @@ QFA_PV_FP4 = 2
 EXPORTS = (
     "qfa_quantize_qk4", "qfa_quantize_v8", "qfa_fwd_prefill", "qfa_fwd_decode",
     "qfa_decode_workspace_bytes", "qfa_decode_default_splits", "qfa_exp2_scale", "qfa_kv_append",
-    "qfa_fwd_prefill_ex", "qfa_fwd_decode_ex",
+    "qfa_fwd_prefill_ex", "qfa_fwd_decode_ex", "qfa_quantize_v4",
     "qfa_status_string", "qfa_version",
 )
 
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.qfa_quantize_qk4.argtypes = [P, I, I, I, I, I, I, F, P, P, P, P]
         L.qfa_quantize_v8.restype = I
         L.qfa_quantize_v8.argtypes = [P, I, I, I, I, I, P, P, P]
+        L.qfa_quantize_v4.restype = I
+        L.qfa_quantize_v4.argtypes = [P, I, I, I, I, I, P, P, P]
         L.qfa_fwd_prefill.restype = I
         L.qfa_fwd_prefill.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, P, P]
         L.qfa_fwd_decode.restype = I
@@ -138,6 +140,11 @@ def qfa_quantize_qk4(x, B, H, S, D, block_size, smooth, prescale, codes, scales,
 
 def qfa_quantize_v8(v, B, H, S, D, block_size, codes, scales, stream=None):
     _check("qfa_quantize_v8", lib().qfa_quantize_v8(_ptr(_u16(v)), B, H, S, D, block_size, _ptr(codes),
+                                                    _ptr(scales), _stream(stream)))
+
+
+def qfa_quantize_v4(v, B, H, S, D, block_size, codes, scales, stream=None):
+    _check("qfa_quantize_v4", lib().qfa_quantize_v4(_ptr(_u16(v)), B, H, S, D, block_size, _ptr(codes),
                                                     _ptr(scales), _stream(stream)))
 
 
@@ -227,6 +234,16 @@ def quantize_v8(v: torch.Tensor, stream=None):
     codes = torch.empty((B, H, nb, D, 32), dtype=torch.uint8, device=v.device)
     scales = torch.empty((B, H, nb, D), dtype=torch.uint8, device=v.device)
     qfa_quantize_v8(v, B, H, S, D, 32, codes, scales, stream)
+    return codes, scales
+
+
+def quantize_v4(v: torch.Tensor, stream=None):
+    """v bf16 [B,H,S,D] -> MXFP4 (codes u8 [B,H,ceil(S/32),D,16], scales u8 [B,H,ceil(S/32),D])."""
+    B, H, S, D = v.shape
+    nb = (S + 31) // 32
+    codes = torch.empty((B, H, nb, D, 16), dtype=torch.uint8, device=v.device)
+    scales = torch.empty((B, H, nb, D), dtype=torch.uint8, device=v.device)
+    qfa_quantize_v4(v, B, H, S, D, 32, codes, scales, stream)
     return codes, scales
 
 

@@ -69,6 +69,15 @@ qfa_status qfa_quantize_v8(const uint16_t* v, int B, int H, int S, int D, int bl
   return from_hip(qfa::launch_quant_v8(v, B, H, S, D, codes, scales, stream));
 }
 
+qfa_status qfa_quantize_v4(const uint16_t* v, int B, int H, int S, int D, int block_size, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream) {
+  if (block_size != 32 || !qk_dim_ok(D)) return QFA_ERR_UNSUPPORTED;
+  if (B < 0 || H < 0 || S < 0 || (long long)B * H > 65535) return QFA_ERR_INVALID_ARG;
+  if ((long long)B * H * S == 0) return QFA_OK;
+  if (!v || !codes || !scales || !aligned16(v) || !aligned16(codes)) return QFA_ERR_INVALID_ARG;
+  return from_hip(qfa::launch_quant_v4(v, B, H, S, D, codes, scales, stream));
+}
+
 static qfa_status check_attn_common(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
                                     const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8,
                                     const uint8_t* v8s, int B, int Hq, int Hkv, int D, float softmax_scale,
@@ -90,10 +99,8 @@ static qfa_status check_attn_common(const uint8_t* q4, const uint8_t* q4s, const
   return QFA_OK;
 }
 
-// QFA_PV_FP8 and QFA_PV_FP8_BLOCKP run; QFA_PV_FP4 is declared, not run.
 static qfa_status check_pv_format(int pv_format) {
-  if (pv_format == QFA_PV_FP8 || pv_format == QFA_PV_FP8_BLOCKP) return QFA_OK;
-  if (pv_format == QFA_PV_FP4) return QFA_ERR_UNSUPPORTED;
+  if (pv_format == QFA_PV_FP8 || pv_format == QFA_PV_FP8_BLOCKP || pv_format == QFA_PV_FP4) return QFA_OK;
   return QFA_ERR_INVALID_ARG;
 }
 

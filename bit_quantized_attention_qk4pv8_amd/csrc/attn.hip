@@ -16,7 +16,7 @@ namespace qfa {
 // = query head g*G + 32*rc + n.  Writes normalised partials to the workspace.
 template <int D, bool COMP, int PV>
 __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
-  using TL = TileLayout<D>;
+  using TL = TileLayout<D, PV>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int g_lane = lane >> 5, n = lane & 31;
@@ -40,7 +40,7 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
 
   RowState<D> st;
   const size_t qrow = (size_t)b * a.Hq + (rvalid ? h : 0);
-  load_q<D>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * (D / 32) : nullptr,
+  load_q<D, PV>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * (D / 32) : nullptr,
             a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid);
 
   uint8_t* bufs = smem;
@@ -48,9 +48,9 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
   for (int o = threadIdx.x * 16; o < 2 * TL::STRIDE; o += blockDim.x * 16)
     *reinterpret_cast<uint4*>(bufs + o) = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
-  TileLoader<D, 1> ld;
+  TileLoader<D, 1, PV> ld;
   ld.init(a.k4, a.k4s, a.v8, a.v8s, (size_t)bg, Lmax, L, 0);
-  LaneOffs<D> lo;
+  LaneOffs<D, PV> lo;
   lo.init();
   if (t0 < t1) {
     ld.issue_k(t0, bufs + (t0 & 1) * TL::STRIDE, 0);
@@ -73,18 +73,18 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
     }
     uint8_t* buf = bufs + (t & 1) * TL::STRIDE;
     v16f s[4];
-    v8i pb[2];
+    POp<PV> pb[2];
     int pscale[2];
-    qk_tile<D>(st, lo, buf, s);
+    qk_tile<D, PV>(st, lo, buf, s);
     softmax_tile<D, COMP, PV>(st, s, t, kTile * t + kTile > L, L - 1, d32, pb, pscale);
-    pv_tile<D>(st, lo, buf + TL::V_OFF, pb, pscale);
+    pv_tile<D, PV>(st, lo, buf + TL::V_OFF, pb, pscale);
     wait_vmem_all();
     if (t + 1 < t1) ld.fixup(t + 1, bufs + ((t + 1) & 1) * TL::STRIDE);
     __syncthreads();
   }
   if (!rvalid) return;
   const size_t prow = ((size_t)b * a.Hq + h) * S + s;
-  store_row<D>(st, a.O + prow * D, a.lse + prow);
+  store_row<D, PV>(st, a.O + prow * D, a.lse + prow);
 }
 
 // LSE merge: one wave per (b, h) row.  LSE = log sum_s e^{LSE_s};  O = sum_s e^{LSE_s - LSE} O_s.
@@ -116,29 +116,34 @@ __global__ void __launch_bounds__(256) k_decode_merge(const float* __restrict__ 
   if (lse && lane == 0) lse[row] = (den > 0.0f) ? mx + __logf(den) : -__builtin_inff();
 }
 
-template <int D>
-static hipError_t decode_d(const AttnArgs& a, float* O, float* lse, hipStream_t s) {
-  using TL = TileLayout<D>;
+template <int D, int PV>
+static hipError_t decode_dp(const AttnArgs& a, float* O, float* lse, hipStream_t s) {
+  using TL = TileLayout<D, PV>;
   const int nrc = (a.G + 31) / 32;
   const long long nwg = (long long)a.B * a.Hkv * nrc * a.num_splits;
   if (nwg == 0) return hipSuccess;
   const bool comp = a.kbar != nullptr;
   const size_t lds = 2 * TL::STRIDE + (comp ? 32 * 32 * 4 : 0);
-#define QFA_SPLIT(C, PVF) hipLaunchKernelGGL((k_decode_split<D, C, PVF>), dim3((unsigned)nwg), dim3(64), lds, s, a, nrc)
-  if (a.pv == PV_FP8) {
-    if (comp) QFA_SPLIT(true, PV_FP8); else QFA_SPLIT(false, PV_FP8);
-  } else if (a.pv == PV_FP8_BLOCKP) {
-    if (comp) QFA_SPLIT(true, PV_FP8_BLOCKP); else QFA_SPLIT(false, PV_FP8_BLOCKP);
-  } else {
-    return hipErrorInvalidValue;
-  }
-#undef QFA_SPLIT
+  if (comp)
+    hipLaunchKernelGGL((k_decode_split<D, true, PV>), dim3((unsigned)nwg), dim3(64), lds, s, a, nrc);
+  else
+    hipLaunchKernelGGL((k_decode_split<D, false, PV>), dim3((unsigned)nwg), dim3(64), lds, s, a, nrc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = a.B * a.Hq;
   hipLaunchKernelGGL(k_decode_merge<D>, dim3((rows + 3) / 4), dim3(256), 0, s, a.O, a.lse, rows, a.num_splits, O,
                      lse);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t decode_d(const AttnArgs& a, float* O, float* lse, hipStream_t s) {
+  switch (a.pv) {
+    case PV_FP8: return decode_dp<D, PV_FP8>(a, O, lse, s);
+    case PV_FP8_BLOCKP: return decode_dp<D, PV_FP8_BLOCKP>(a, O, lse, s);
+    case PV_FP4: return decode_dp<D, PV_FP4>(a, O, lse, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_decode(const AttnArgs& a, float* O, float* lse, hipStream_t s) {

@@ -16,21 +16,38 @@
 // rounded P codes (same tutorial, section "Direct-P").
 #pragma once
 
+#include <type_traits>
+
 #include "qfa_internal.h"
 
 namespace qfa {
 
 // LDS image of one K/V tile (128 keys):
 //   K region [K codes 128 x D/2][K scales, 1 KB area]
-//   V region [V codes 4 x D x 32][V scales, 1 KB area]
+//   V region [V codes 4 x D x VR][V scales, 1 KB area]  (VR = 32 bytes per
+//            (32-token block, channel) record in E4M3, 16 in MXFP4)
 // The two regions may live in separate buffers (KREG / VREG bytes each).
 // K and V codes are stored with an XOR swizzle of their 16-byte chunks (see
 // kswz / vswz) so that the MFMA operand reads are free of bank conflicts.
-template <int D>
+// P/V formats.  PV_FP8 is the method: P = E4M3(256 * 2^(y - m)) with one
+// power-of-two scale per row (the running max m) and V in E4M3.
+// PV_FP8_BLOCKP gives P one E8M0 scale per (row, 32 keys): block b is coded
+// as E4M3(256 * 2^(y - e_b)) with e_b = max(ceil(max_{j in b} y_j), m - 64)
+// and weighted 2^(e_b - m_ref) through the MFMA's scale operand.  PV_FP4
+// codes P the same way in E2M1 (E2M1(4 * 2^(y - e_b))) and takes V in MXFP4,
+// and both products run on the FP4 MFMA.  ([FA4tut] "Direct-P": one E8M0
+// scale per 32 probabilities; [MpFA] abstract: FP8 P/V versus fully FP4
+// attention.)
+constexpr int PV_FP8 = 0, PV_FP8_BLOCKP = 1, PV_FP4 = 2;
+// V bytes per (32-token block, channel) record
+template <int PV>
+constexpr int v_record() { return PV == PV_FP4 ? 16 : 32; }
+
+template <int D, int PV = PV_FP8>
 struct TileLayout {
   static constexpr int KC = kTile * D / 2;
   static constexpr int KS_BYTES = kTile * D / 32;
-  static constexpr int VC = kTile * D;
+  static constexpr int VC = (kTile / 32) * D * v_record<PV>();
   static constexpr int VS_BYTES = (kTile / 32) * D;
   static constexpr int K_OFF = 0;
   static constexpr int KS_OFF = KC;
@@ -48,6 +65,16 @@ struct TileLayout {
 // Token of MFMA row rho inside a 32-token block: lane group g = (rho/4)%2 of
 // the S^T output then holds tokens 16g .. 16g+15 in register order.
 __device__ __forceinline__ int perm_token(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
+// PV_FP4: MFMA c = 2h + w of a tile covers, for lane group g, keys
+// 64h + 32g + 16w .. +15, so a lane holds all 32 keys of block 2h + g (the
+// FP4 P operand of one lane is one whole 32-key block).  Row rho reads token
+// 64h + 16w + perm64(rho).
+__device__ __forceinline__ int perm64(int rho) { return 32 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
+// Key (from the tile start) of score s[c][rr] in lane group g.
+template <int PV>
+__device__ __forceinline__ int score_key(int c, int g, int rr) {
+  return PV == PV_FP4 ? 64 * (c >> 1) + 32 * g + 16 * (c & 1) + rr : 32 * c + 16 * g + rr;
+}
 
 // K row of token tok (D/2 bytes): chunk k is stored at k ^ kswz(tok).
 template <int D>
@@ -71,9 +98,10 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // tile and V blocks past the end, no read leaves the slice, and the per-lane
 // voffsets (which carry the LDS swizzle) stay loop-invariant, so issuing a
 // tile costs no VALU work.
-template <int D, int NW>
+template <int D, int NW, int PV = PV_FP8>
 struct TileLoader {
-  using TL = TileLayout<D>;
+  using TL = TileLayout<D, PV>;
+  static constexpr int VR = v_record<PV>();
   const uint8_t* kc;  // slice bases
   const uint8_t* ks;
   const uint8_t* vc;
@@ -89,11 +117,11 @@ struct TileLoader {
     L = L_valid;
     kc = k4 + bg * L_storage * (D / 2);
     ks = k4s + bg * L_storage * (D / 32);
-    vc = v8 + bg * nvb_storage * D * 32;
+    vc = v8 + bg * nvb_storage * D * VR;
     vs = v8s + bg * nvb_storage * D;
     kc_bytes = (uint32_t)L_valid * (D / 2);
     ks_bytes = (uint32_t)L_valid * (D / 32);
-    vc_bytes = (uint32_t)nvb * D * 32;
+    vc_bytes = (uint32_t)nvb * D * VR;
     vs_bytes = (uint32_t)nvb * D;
   }
 
@@ -112,8 +140,12 @@ struct TileLoader {
       vk0 = vk1 = tl * 32 + 16 * (kpos ^ kswz<D>(tl));
     }
     vkw = (wave & 1) ? vk1 : vk0;
-    const int rl = p >> 1, hpos = p & 1;  // 32 records of 32 B per KB; vswz uses record bits 2, 3
-    vv = rl * 32 + 16 * (hpos ^ vswz(rl));
+    if (PV == PV_FP4) {  // 64 records of 16 B per KB, not swizzled
+      vv = p * 16;
+    } else {             // 32 records of 32 B per KB; vswz uses record bits 2, 3
+      const int rl = p >> 1, hpos = p & 1;
+      vv = rl * 32 + 16 * (hpos ^ vswz(rl));
+    }
   }
 
   // Resource for the bytes [off, bytes) of a slice region (empty when off >=
@@ -236,23 +268,38 @@ __device__ __forceinline__ int kblock(int g, int k) { return D == 128 ? 2 * g + 
 // Per-lane LDS byte offsets of a wave's operand reads, relative to a tile's K
 // or V region; the compile-time part of each address goes into the
 // instruction's offset field, so a read costs no VALU work.
-template <int D>
+template <int D, int PV = PV_FP8>
 struct LaneOffs {
-  uint32_t k[D / 64];  // K fragment of MFMA k; key block c adds 32c * D/2
-  uint32_t ks;         // K scale bytes (KC included); key block c adds 32c * D/32
-  uint32_t v;          // V fragment; (half h, part w, channel block cb) adds ((2h + w) * D + 32cb) * 32
-  uint32_t vs;         // V scale byte (VC included); adds 2h * D + 32cb
+  // K fragment of MFMA k.  E4M3 P: key block c adds 32c * D/2.  PV_FP4: MFMA
+  // c = 2h + w adds (64h + 16w) * D/2 to k1 (w = 1) or k (w = 0): adding 16
+  // flips token bit 4, which the K swizzle uses.
+  uint32_t k[D / 64];
+  uint32_t k1[PV == PV_FP4 ? D / 64 : 1];
+  uint32_t ks;  // K scale bytes (KC included); key block c adds 32c * D/32 (PV_FP4: (64h + 16w) * D/32)
+  // V fragment.  E4M3: (half h, part w, channel block cb) adds ((2h + w) * D + 32cb) * 32.
+  // MXFP4: the lane's whole record of block 2h + g; (h, cb) adds (2h * D + 32cb) * 16.
+  uint32_t v;
+  uint32_t vs;  // V scale byte (VC included); adds 2h * D + 32cb
 
   __device__ __forceinline__ void init() {
-    using TL = TileLayout<D>;
+    using TL = TileLayout<D, PV>;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 5, rho = lane & 31;
-    const int tok = perm_token(rho);  // kswz depends on token bits 1, 2, 4 only: the same for every key block
+    // kswz depends on token bits 1, 2, 4 only: for the E4M3 formats the same for every key block
+    const int tok = PV == PV_FP4 ? perm64(rho) : perm_token(rho);
     const int sw = kswz<D>(tok);
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) this->k[k] = tok * (D / 2) + 16 * (kblock<D>(g, k) ^ sw);
+    if constexpr (PV == PV_FP4) {
+      const int sw1 = kswz<D>(tok + 16);
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) k1[k] = tok * (D / 2) + 16 * (kblock<D>(g, k) ^ sw1);
+    }
     ks = TL::KC + tok * (D / 32) + (D == 128 ? 2 * g : g);
-    v = rho * 32 + 16 * (g ^ vswz(rho));  // vswz depends on channel bits 2, 3 only
+    if (PV == PV_FP4)
+      v = (g * D + rho) * 16;
+    else
+      v = rho * 32 + 16 * (g ^ vswz(rho));  // vswz depends on channel bits 2, 3 only
     vs = TL::VC + g * D + rho;
   }
 };
@@ -266,16 +313,13 @@ struct RowState {
   v16f lv;         // denominator 1 . P^T (every element equals the row sum), in the m_ref frame
   float m;         // running max in log2 units, on the integer grid (-inf before any key)
   float m_ref;     // frame of o and lv: both hold sum 2^(m_t - m_ref) P_t (V_t | 1)
-  v8i ones;        // FP8 1.0 in every byte: the A operand of the denominator product
+  v8i ones;        // 1.0 in every element (E4M3 0x38, or E2M1 0x2 in the first four dwords): the A
+                   // operand of the denominator product
 };
 
-// P/V formats.  PV_FP8 is the method: P = E4M3(256 * 2^(y - m)) with one
-// power-of-two scale per row (the running max m).  PV_FP8_BLOCKP gives P one
-// E8M0 scale per (row, 32 keys): block b is coded as E4M3(256 * 2^(y - e_b))
-// with e_b = max(ceil(max_{j in b} y_j), m - 64) and weighted 2^(e_b - m_ref)
-// through the MFMA's scale operand.  ([FA4tut] "Direct-P": one E8M0 scale per
-// 32 probabilities; [MpFA] abstract: FP8 P versus fully FP4 attention.)
-constexpr int PV_FP8 = 0, PV_FP8_BLOCKP = 1;
+// The P and V operand types of the P V product: 32 E4M3 bytes or 32 E2M1 nibbles per lane.
+template <int PV>
+using POp = typename std::conditional<PV == PV_FP4, v4i, v8i>::type;
 
 // Softmax step of one tile.  s holds S' = Q'K^T, the logits in log2 units
 // (Q carries the factor softmax_scale * log2 e).  Masks keys > jlim (when
@@ -284,22 +328,22 @@ constexpr int PV_FP8 = 0, PV_FP8_BLOCKP = 1;
 // into pb, the B operand of the P V product (pb[h] covers keys 64h .. 64h+63).
 // pscale[h] receives the E8M0 code that the P V product of half h applies:
 // 2^(m - m_ref) (PV_FP8), or 2^(e_b - m_ref) of the key block b = 2h + g
-// whose scale this lane supplies (PV_FP8_BLOCKP).  O and l are touched only
-// by the rare frame rebase.
+// whose scale this lane supplies (PV_FP8_BLOCKP, PV_FP4).  O and l are
+// touched only by the rare frame rebase.
 template <int D, bool COMP, int PV>
 __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int t, bool need_mask, int jlim,
-                                             float d32, v8i (&pb)[2], int (&pscale)[2]) {
+                                             float d32, POp<PV> (&pb)[2], int (&pscale)[2]) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
-  // ---- mask (diagonal / ragged tiles only); score s[c][rr] is key 128t + 32c + 16g + rr.
-  // A lane's 16 keys of block c are consecutive, so the visible ones are a
-  // prefix rr <= nvm1; the select is done on the bits ((nvm1 - rr) >> 31 is -1
-  // for a masked key), which keeps 64 comparison masks out of the SGPRs.
+  // ---- mask (diagonal / ragged tiles only); score s[c][rr] is key
+  // 128t + score_key(c, g, rr).  A lane's 16 keys of MFMA c are consecutive,
+  // so the visible ones are a prefix rr <= nvm1; the select is done on the
+  // bits ((nvm1 - rr) >> 31 is -1 for a masked key), which keeps 64
+  // comparison masks out of the SGPRs.
   if (need_mask) {
-    const int jb = kTile * t + 16 * g;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int nvm1 = jlim - (jb + 32 * c);
+      const int nvm1 = jlim - (kTile * t + score_key<PV>(c, g, 0));
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int msk = (nvm1 - rr) >> 31;
@@ -317,8 +361,23 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
   // ---- row max (two left-associated chains: max(max(m, a), b) compiles to
   // v_max3_f32, one instruction per two scores) and one lane swap
   float mx;
-  float bmax[4];  // PV_FP8_BLOCKP: max of key block c (both lanes of the row)
-  if constexpr (PV == PV_FP8) {
+  float bmax[4];  // PV_FP8_BLOCKP: max of key block c (both lanes of the row); PV_FP4: [h] of block 2h + g
+  if constexpr (PV == PV_FP4) {
+    // a lane holds all 32 keys of block 2h + g: its max needs no other lane
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float x = __builtin_fmaxf(s[2 * h][0], s[2 * h][1]);
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int rr = (w == 0 ? 2 : 0); rr < 16; rr += 2)
+          x = __builtin_fmaxf(__builtin_fmaxf(x, s[2 * h + w][rr]), s[2 * h + w][rr + 1]);
+      bmax[h] = x;
+    }
+    mx = __builtin_fmaxf(bmax[0], bmax[1]);
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  } else if constexpr (PV == PV_FP8) {
     float mx0 = s[0][0], mx1 = s[2][0];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -383,7 +442,14 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
   // that can give a non-zero code (y > e - 18) have 2^y in [2^-118, 2^100].
   // A wave with an exponent outside subtracts it from the scores first.
   float e[4];
-  if constexpr (PV == PV_FP8) {
+  if constexpr (PV == PV_FP4) {  // e[c]: the exponent of MFMA c's keys (block 2h + g for c = 2h + w)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float eh = (mn == -__builtin_inff()) ? 0.0f : __builtin_fmaxf(__builtin_ceilf(bmax[h]), mn - 64.0f);
+      e[2 * h] = e[2 * h + 1] = eh;
+      pscale[h] = (mn == -__builtin_inff()) ? kScaleOne : kScaleOne + (int)(eh - st.m_ref);
+    }
+  } else if constexpr (PV == PV_FP8) {
     pscale[0] = pscale[1] = (mn == -__builtin_inff()) ? kScaleOne : kScaleOne + (int)(mn - st.m_ref);
     e[0] = e[1] = e[2] = e[3] = (mn == -__builtin_inff()) ? 0.0f : mn;
   } else {
@@ -409,9 +475,32 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) s[c][rr] -= e[c];
   }
+  // the conversion's scale: 2^(e - 8) for E4M3 (codes 256 * 2^(y - e)),
+  // 2^(e - 2) for E2M1 (codes 4 * 2^(y - e))
+  constexpr int PB = PV == PV_FP4 ? 2 : 8;
   float cs[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) cs[c] = far ? 0x1p-8f : __builtin_ldexpf(1.0f, (int)e[c] - 8);
+  for (int c = 0; c < 4; ++c) cs[c] = far ? (PV == PV_FP4 ? 0x1p-2f : 0x1p-8f) : __builtin_ldexpf(1.0f, (int)e[c] - PB);
+  if constexpr (PV == PV_FP4) {
+    // pb[h] register r holds keys 8r .. 8r+7 of block 2h + g (s[2h + r/2][8(r%2) ..]),
+    // two E2M1 codes per byte, the lower key in the low nibble
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 2 * h + (r >> 1), r0 = 8 * (r & 1);
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(s[c][r0 + j]);
+        uint32_t w = __float_as_uint(p[0]);  // dead old value: every byte is written
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[0], p[1], cs[c], 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[2], p[3], cs[c], 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[4], p[5], cs[c], 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[6], p[7], cs[c], 3);
+        pb[h][r] = (int)w;
+      }
+    return;
+  } else {
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -428,6 +517,7 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
       w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p2, p3, cs[c], true);
       pb[h][k] = __builtin_bit_cast(int, w);
     }
+  }
 }
 
 // One K operand block (32 keys x all channels): the A operands of the D/64
@@ -438,15 +528,19 @@ struct KBlk {
   int sc;
 };
 
-template <int D>
-__device__ __forceinline__ void load_k_blk(const uint8_t* kreg, const LaneOffs<D>& lo, int c, KBlk<D>& k) {
+template <int D, int PV>
+__device__ __forceinline__ void load_k_blk(const uint8_t* kreg, const LaneOffs<D, PV>& lo, int c, KBlk<D>& k) {
+  // first token of MFMA c's rows (plus the lane's own token offset)
+  const int t0 = PV == PV_FP4 ? 64 * (c >> 1) + 16 * (c & 1) : 32 * c;
 #pragma unroll
-  for (int kk = 0; kk < D / 64; ++kk)
-    k.ka[kk] = *reinterpret_cast<const v4i*>(kreg + lo.k[kk] + 32 * c * (D / 2));
+  for (int kk = 0; kk < D / 64; ++kk) {
+    const uint32_t lk = (PV == PV_FP4 && (c & 1)) ? lo.k1[PV == PV_FP4 ? kk : 0] : lo.k[kk];
+    k.ka[kk] = *reinterpret_cast<const v4i*>(kreg + lk + t0 * (D / 2));
+  }
   if (D == 128)
-    k.sc = *reinterpret_cast<const uint16_t*>(kreg + lo.ks + 32 * c * (D / 32));
+    k.sc = *reinterpret_cast<const uint16_t*>(kreg + lo.ks + t0 * (D / 32));
   else
-    k.sc = kreg[lo.ks + 32 * c * (D / 32)];
+    k.sc = kreg[lo.ks + t0 * (D / 32)];
 }
 
 // S^T block c = K_c Q^T: sc_[rr] is the score of this lane's row (l % 32)
@@ -460,13 +554,34 @@ __device__ __forceinline__ void qk_blk(const RowState<D>& st, const KBlk<D>& k, 
 
 // One V operand (64 keys x 32 channels: half h = q / (D/32), channel block
 // cb = q % (D/32)) and its E8M0 scale byte.
-template <int D>
-__device__ __forceinline__ void load_v_op(const uint8_t* vreg, const LaneOffs<D>& lo, int q, v8i& a, int& sa) {
+template <int D, int PV>
+__device__ __forceinline__ void load_v_op(const uint8_t* vreg, const LaneOffs<D, PV>& lo, int q, POp<PV>& a,
+                                          int& sa) {
   const int h = q / (D / 32), cb = q % (D / 32);
-  const v4i a0 = *reinterpret_cast<const v4i*>(vreg + lo.v + ((2 * h) * D + 32 * cb) * 32);
-  const v4i a1 = *reinterpret_cast<const v4i*>(vreg + lo.v + ((2 * h + 1) * D + 32 * cb) * 32);
-  a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  if constexpr (PV == PV_FP4) {
+    a = *reinterpret_cast<const v4i*>(vreg + lo.v + (2 * h * D + 32 * cb) * 16);
+  } else {
+    const v4i a0 = *reinterpret_cast<const v4i*>(vreg + lo.v + ((2 * h) * D + 32 * cb) * 32);
+    const v4i a1 = *reinterpret_cast<const v4i*>(vreg + lo.v + ((2 * h + 1) * D + 32 * cb) * 32);
+    a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
   sa = vreg[lo.vs + 2 * h * D + 32 * cb];
+}
+
+// O^T or l += V^T P^T of one (half, channel block) on the FP8 or the FP4 MFMA.
+template <int PV>
+__device__ __forceinline__ v16f mfma_pv(const POp<PV>& a, const POp<PV>& b, v16f c, int sa, int sb) {
+  if constexpr (PV == PV_FP4)
+    return mfma_fp4_32x32x64(a, b, c, sa, sb);
+  else
+    return mfma_fp8_32x32x64(a, b, c, sa, sb);
+}
+template <int PV>
+__device__ __forceinline__ POp<PV> ones_op(const v8i& ones) {
+  if constexpr (PV == PV_FP4)
+    return v4i{ones[0], ones[1], ones[2], ones[3]};
+  else
+    return ones;
 }
 
 // O^T += 2^(m - m_ref) V^T P^T of one tile (FP8 x FP8; V's E8M0 scale per 32
@@ -483,79 +598,80 @@ struct NoHook {
 // hook(k) runs after the k-th MFMA step (k = 0 .. 2 D/32 + 3), inside the
 // scheduling fences: a place for instructions that should issue while the
 // matrix unit is busy.
-template <int D, class Hook = NoHook>
-__device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D>& lo, const uint8_t* vreg,
-                                           const v8i (&pb)[2], const int (&pscale)[2], const uint8_t* kreg,
+template <int D, int PV, class Hook = NoHook>
+__device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV>& lo, const uint8_t* vreg,
+                                           const POp<PV> (&pb)[2], const int (&pscale)[2], const uint8_t* kreg,
                                            v16f (&s)[4], const Hook& hook = Hook()) {
   constexpr int NQ = 2 * (D / 32);  // P V products (excluding the denominator)
   constexpr int R = 3;              // V operands in flight
-  v8i va[R];
+  POp<PV> va[R];
   int vs[R];
   KBlk<D> kb[2];
 #pragma unroll
-  for (int q = 0; q < R; ++q) load_v_op<D>(vreg, lo, q, va[q], vs[q]);
+  for (int q = 0; q < R; ++q) load_v_op<D, PV>(vreg, lo, q, va[q], vs[q]);
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     __builtin_amdgcn_sched_barrier(0);
     const int h = q / (D / 32), cb = q % (D / 32);
-    st.o[cb] = mfma_fp8_32x32x64(va[q % R], pb[h], st.o[cb], vs[q % R], pscale[h]);
-    if (cb == D / 32 - 1) st.lv = mfma_fp8_32x32x64(st.ones, pb[h], st.lv, kScaleOne, pscale[h]);
+    st.o[cb] = mfma_pv<PV>(va[q % R], pb[h], st.o[cb], vs[q % R], pscale[h]);
+    if (cb == D / 32 - 1) st.lv = mfma_pv<PV>(ones_op<PV>(st.ones), pb[h], st.lv, kScaleOne, pscale[h]);
     if (q + R < NQ)
-      load_v_op<D>(vreg, lo, q + R, va[q % R], vs[q % R]);
+      load_v_op<D, PV>(vreg, lo, q + R, va[q % R], vs[q % R]);
     else if (q + R - NQ < 2)
-      load_k_blk<D>(kreg, lo, q + R - NQ, kb[q + R - NQ]);
+      load_k_blk<D, PV>(kreg, lo, q + R - NQ, kb[q + R - NQ]);
     hook(q);
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     __builtin_amdgcn_sched_barrier(0);
     qk_blk<D>(st, kb[c & 1], s[c]);
-    if (c + 2 < 4) load_k_blk<D>(kreg, lo, c + 2, kb[c & 1]);
+    if (c + 2 < 4) load_k_blk<D, PV>(kreg, lo, c + 2, kb[c & 1]);
     hook(NQ + c);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // P V of one tile alone, pipelined like pv_then_qk.
-template <int D>
-__device__ __forceinline__ void pv_tile(RowState<D>& st, const LaneOffs<D>& lo, const uint8_t* vreg,
-                                        const v8i (&pb)[2], const int (&pscale)[2]) {
+template <int D, int PV>
+__device__ __forceinline__ void pv_tile(RowState<D>& st, const LaneOffs<D, PV>& lo, const uint8_t* vreg,
+                                        const POp<PV> (&pb)[2], const int (&pscale)[2]) {
   constexpr int NQ = 2 * (D / 32);
   constexpr int R = 3;
-  v8i va[R];
+  POp<PV> va[R];
   int vs[R];
 #pragma unroll
-  for (int q = 0; q < R; ++q) load_v_op<D>(vreg, lo, q, va[q], vs[q]);
+  for (int q = 0; q < R; ++q) load_v_op<D, PV>(vreg, lo, q, va[q], vs[q]);
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     __builtin_amdgcn_sched_barrier(0);
     const int h = q / (D / 32), cb = q % (D / 32);
-    st.o[cb] = mfma_fp8_32x32x64(va[q % R], pb[h], st.o[cb], vs[q % R], pscale[h]);
-    if (cb == D / 32 - 1) st.lv = mfma_fp8_32x32x64(st.ones, pb[h], st.lv, kScaleOne, pscale[h]);
-    if (q + R < NQ) load_v_op<D>(vreg, lo, q + R, va[q % R], vs[q % R]);
+    st.o[cb] = mfma_pv<PV>(va[q % R], pb[h], st.o[cb], vs[q % R], pscale[h]);
+    if (cb == D / 32 - 1) st.lv = mfma_pv<PV>(ones_op<PV>(st.ones), pb[h], st.lv, kScaleOne, pscale[h]);
+    if (q + R < NQ) load_v_op<D, PV>(vreg, lo, q + R, va[q % R], vs[q % R]);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // S = K Q^T of one tile alone, two K blocks in flight.
-template <int D>
-__device__ __forceinline__ void qk_tile(const RowState<D>& st, const LaneOffs<D>& lo, const uint8_t* kreg,
+template <int D, int PV>
+__device__ __forceinline__ void qk_tile(const RowState<D>& st, const LaneOffs<D, PV>& lo, const uint8_t* kreg,
                                         v16f (&s)[4]) {
   KBlk<D> kb[2];
-  load_k_blk<D>(kreg, lo, 0, kb[0]);
-  load_k_blk<D>(kreg, lo, 1, kb[1]);
+  load_k_blk<D, PV>(kreg, lo, 0, kb[0]);
+  load_k_blk<D, PV>(kreg, lo, 1, kb[1]);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     __builtin_amdgcn_sched_barrier(0);
     qk_blk<D>(st, kb[c & 1], s[c]);
-    if (c + 2 < 4) load_k_blk<D>(kreg, lo, c + 2, kb[c & 1]);
+    if (c + 2 < 4) load_k_blk<D, PV>(kreg, lo, c + 2, kb[c & 1]);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Epilogue of one row: O = O^T / l (this lane writes half of the row's
-// channels) and LSE = ln2 * (m_ref + log2(l / 256)).  lse_row may be null.
-template <int D>
+// channels) and LSE = ln2 * (m_ref + log2(l / 256)) (E4M3 P: codes of
+// 256 * 2^(y - e); E2M1 P: 4 * 2^(y - e), so l / 4).  lse_row may be null.
+template <int D, int PV = PV_FP8>
 __device__ __forceinline__ void store_row(const RowState<D>& st, float* orow, float* lse_row) {
   const int g = (threadIdx.x & 63) >> 5;
   const float l = st.lv[0];
@@ -566,7 +682,8 @@ __device__ __forceinline__ void store_row(const RowState<D>& st, float* orow, fl
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) orow[32 * cb + (rr >> 2) * 8 + 4 * g + (rr & 3)] = st.o[cb][rr] * inv;
   if (lse_row && g == 0)
-    *lse_row = empty ? -__builtin_inff() : 0.69314718055994531f * (st.m_ref + __builtin_log2f(l * 0x1p-8f));
+    *lse_row = empty ? -__builtin_inff()
+                     : 0.69314718055994531f * (st.m_ref + __builtin_log2f(l * (PV == PV_FP4 ? 0x1p-2f : 0x1p-8f)));
 }
 
 // delta^T for 32 tiles starting at tau0: Kbar[tau0 .. tau0+31] . Q_bf16^T,
@@ -615,7 +732,7 @@ __device__ __forceinline__ void compute_delta(float* dl, const uint16_t* kbar_bg
 // With q4row null, the row is quantised here from its bf16 values qbfrow
 // (times c2, then the MXFP4 block rule): the same bytes the quantiser kernel
 // writes for Q with prescale c2.
-template <int D>
+template <int D, int PV = PV_FP8>
 __device__ __forceinline__ void load_q(RowState<D>& st, const uint8_t* q4row, const uint8_t* q4srow,
                                        const uint16_t* qbfrow, float c2, bool valid) {
   const int g = (threadIdx.x & 63) >> 5;
@@ -645,7 +762,8 @@ __device__ __forceinline__ void load_q(RowState<D>& st, const uint8_t* q4row, co
   st.lv = v16f{};
   st.m = -__builtin_inff();
   st.m_ref = -__builtin_inff();
-  st.ones = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  constexpr int one = PV == PV_FP4 ? 0x22222222 : 0x38383838;  // E2M1 / E4M3 1.0 in every element
+  st.ones = v8i{one, one, one, one, one, one, one, one};
   asm volatile("" : "+v"(st.ones));  // resident in VGPRs for the whole loop (no per-tile rebuild)
 }
 

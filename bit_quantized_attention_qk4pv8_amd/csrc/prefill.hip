@@ -82,7 +82,7 @@ __device__ __forceinline__ void window_barrier() {
 
 template <int D, bool COMP, int PV>
 __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) {
-  using TL = TileLayout<D>;
+  using TL = TileLayout<D, PV>;
   constexpr int NB = kPrefillBuffers;  // LDS buffers per operand
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -153,16 +153,16 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   for (int o = threadIdx.x * 16; o < NB * (TL::KREG + TL::VREG); o += blockDim.x * 16)
     *reinterpret_cast<uint4*>(smem + o) = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
-  TileLoader<D, 8> ld;  // all 8 waves share the DMA
+  TileLoader<D, 8, PV> ld;  // all 8 waves share the DMA
   ld.init(a.k4, a.k4s, a.v8, a.v8s, (size_t)grp, L, L, wave);
-  LaneOffs<D> lo;
+  LaneOffs<D, PV> lo;
   lo.init();
-  constexpr int SLOTS = TileLoader<D, 8>::SLOTS;  // code DMA instructions per wave and window
+  constexpr int SLOTS = TileLoader<D, 8, PV>::SLOTS;  // code DMA instructions per wave and window
   // K(0 .. NB-2), V(0 .. NB-3) before the loop; Q (and its quantisation)
   // while they are in flight
   for (int j = 0; j < NB - 1 && j < T; ++j) ld.issue_k(j, kbuf + j * TL::KREG, wave);
   for (int j = 0; j < NB - 2 && j < T; ++j) ld.issue_v(j, vbuf + j * TL::VREG, wave);
-  load_q<D>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * (D / 32) : nullptr,
+  load_q<D, PV>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * (D / 32) : nullptr,
             a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid);
   wait_vmem_le(0);
   __syncthreads();  // every wave's loads have landed before the scale patch
@@ -172,7 +172,7 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   }
   __syncthreads();
 
-  v8i pb[2];  // P of the last softmax, consumed by the next products
+  POp<PV> pb[2];  // P of the last softmax, consumed by the next products
   int pscale[2] = {kScaleOne, kScaleOne};
   int kb_cur = 0, vb_prev = NB - 1;  // buffer of K(t) and of V(t-1)
 #pragma nounroll
@@ -203,11 +203,11 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
     // (a wave's last P V also computes a product of whatever K buffer kb_cur
     // holds; that S is never used: one code path keeps the register budget)
     if (do_pv) {
-      pv_then_qk<D>(st, lo, vbuf + vb_prev * TL::VREG, pb, pscale, kbuf + kb_cur * TL::KREG, s, dma);
+      pv_then_qk<D, PV>(st, lo, vbuf + vb_prev * TL::VREG, pb, pscale, kbuf + kb_cur * TL::KREG, s, dma);
     } else {
 #pragma unroll
       for (int k = 0; k <= SLOTS; ++k) dma(k);
-      if (do_qk) qk_tile<D>(st, lo, kbuf + kb_cur * TL::KREG, s);
+      if (do_qk) qk_tile<D, PV>(st, lo, kbuf + kb_cur * TL::KREG, s);
     }
     __builtin_amdgcn_s_setprio(0);
     // ---- end of this wave's window: its loads of K(t+1) and V(t) (issued
@@ -233,28 +233,33 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
     vb_prev = vb_prev + 1 == NB ? 0 : vb_prev + 1;
   }
 
-  if (rvalid) store_row<D>(st, a.O + qrow * D, a.lse ? a.lse + qrow : nullptr);
+  if (rvalid) store_row<D, PV>(st, a.O + qrow * D, a.lse ? a.lse + qrow : nullptr);
 }
 
-template <int D>
-static hipError_t prefill_d(const AttnArgs& a, hipStream_t s) {
-  using TL = TileLayout<D>;
+template <int D, int PV>
+static hipError_t prefill_dp(const AttnArgs& a, hipStream_t s) {
+  using TL = TileLayout<D, PV>;
   const int U = a.G * ((a.Sq + 63) / 64);
   const int nwg_per_group = (U + 3) / 4;
   const long long nwg = (long long)a.B * a.Hkv * nwg_per_group;
   if (nwg == 0) return hipSuccess;
   const bool comp = a.kbar != nullptr;
   const size_t lds = kPrefillBuffers * (TL::KREG + TL::VREG) + 1024 + (comp ? (size_t)8 * 32 * 32 * 4 : 0);
-#define QFA_PREFILL(C, PVF) hipLaunchKernelGGL((k_prefill<D, C, PVF>), dim3((unsigned)nwg), dim3(512), lds, s, a, nwg_per_group)
-  if (a.pv == PV_FP8) {
-    if (comp) QFA_PREFILL(true, PV_FP8); else QFA_PREFILL(false, PV_FP8);
-  } else if (a.pv == PV_FP8_BLOCKP) {
-    if (comp) QFA_PREFILL(true, PV_FP8_BLOCKP); else QFA_PREFILL(false, PV_FP8_BLOCKP);
-  } else {
-    return hipErrorInvalidValue;
-  }
-#undef QFA_PREFILL
+  if (comp)
+    hipLaunchKernelGGL((k_prefill<D, true, PV>), dim3((unsigned)nwg), dim3(512), lds, s, a, nwg_per_group);
+  else
+    hipLaunchKernelGGL((k_prefill<D, false, PV>), dim3((unsigned)nwg), dim3(512), lds, s, a, nwg_per_group);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t prefill_d(const AttnArgs& a, hipStream_t s) {
+  switch (a.pv) {
+    case PV_FP8: return prefill_dp<D, PV_FP8>(a, s);
+    case PV_FP8_BLOCKP: return prefill_dp<D, PV_FP8_BLOCKP>(a, s);
+    case PV_FP4: return prefill_dp<D, PV_FP4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s) {

@@ -116,6 +116,8 @@ hipError_t launch_quant_qk4(const uint16_t* x, int B, int H, int S, int D, int s
                             uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t s);
 hipError_t launch_quant_v8(const uint16_t* v, int B, int H, int S, int D, uint8_t* codes, uint8_t* scales,
                            hipStream_t s);
+hipError_t launch_quant_v4(const uint16_t* v, int B, int H, int S, int D, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s);
 
 struct AttnArgs {
   const uint8_t* q4;
@@ -133,7 +135,7 @@ struct AttnArgs {
   int causal;
   float c2;               // softmax_scale * log2(e), rounded to binary32
   int num_splits;         // decode
-  int pv;                 // P/V format (PV_FP8, PV_FP8_BLOCKP)
+  int pv;                 // P/V format (PV_FP8, PV_FP8_BLOCKP, PV_FP4)
 };
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);

@@ -133,6 +133,33 @@ __global__ void __launch_bounds__(D) k_quant_v8(const uint16_t* __restrict__ v, 
   fp8_block_store(x, codes + ((bh * nblk + blk) * D + c) * kBlock, scales + (bh * nblk + blk) * D + c);
 }
 
+// V -> MXFP4 along tokens (the full-FP4 contrast case): one workgroup per
+// 32-token block stages it through LDS as for E4M3; thread c quantises channel
+// c's 32 tokens with the Q/K block rule (tokens past S count as 0).
+template <int D>
+__global__ void __launch_bounds__(D) k_quant_v4(const uint16_t* __restrict__ v, int S, int nblk,
+                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ uint16_t tile[kBlock * D];
+  const int blk = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int j0 = blk * kBlock;
+  const int n = min(kBlock, S - j0);
+  const uint16_t* src = v + (bh * (size_t)S + j0) * D;
+  const int chunks = n * D / 8;
+  for (int i = threadIdx.x; i < chunks; i += D)
+    reinterpret_cast<uint4*>(tile)[i] = reinterpret_cast<const uint4*>(src)[i];
+  __syncthreads();
+  const int c = threadIdx.x;
+  float x[kBlock];
+#pragma unroll
+  for (int t = 0; t < kBlock; ++t) x[t] = (t < n) ? bf16_bits_to_float(tile[t * D + c]) : 0.0f;
+  uint4 cd;
+  uint8_t sc;
+  mxfp4_block(x, cd, sc);
+  *reinterpret_cast<uint4*>(codes + ((bh * nblk + blk) * D + c) * (kBlock / 2)) = cd;
+  scales[(bh * nblk + blk) * D + c] = sc;
+}
+
 // ---------------------------------------------------------------- KV-cache writer
 // Appending n tokens to a sequence that holds L: the V records of the 32-token
 // blocks from floor(L/32) on and (with smoothing) every K row of the 128-token
@@ -287,6 +314,21 @@ hipError_t launch_quant_v8(const uint16_t* v, int B, int H, int S, int D, uint8_
     QFA_V8_CASE(32) QFA_V8_CASE(64) QFA_V8_CASE(96) QFA_V8_CASE(128) QFA_V8_CASE(160) QFA_V8_CASE(192)
     QFA_V8_CASE(224) QFA_V8_CASE(256)
 #undef QFA_V8_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_v4(const uint16_t* v, int B, int H, int S, int D, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s) {
+  const int nblk = (S + kBlock - 1) / kBlock;
+  dim3 grid(nblk, B * H);
+  switch (D) {
+#define QFA_V4_CASE(DD) \
+  case DD: hipLaunchKernelGGL(k_quant_v4<DD>, grid, dim3(DD), 0, s, v, S, nblk, codes, scales); break;
+    QFA_V4_CASE(32) QFA_V4_CASE(64) QFA_V4_CASE(96) QFA_V4_CASE(128) QFA_V4_CASE(160) QFA_V4_CASE(192)
+    QFA_V4_CASE(224) QFA_V4_CASE(256)
+#undef QFA_V4_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -100,6 +100,18 @@ qfa_status qfa_quantize_v8(const uint16_t* v, int B, int H, int S, int D, int bl
                            uint8_t* scales, hipStream_t stream);
 
 /*
+ * V quantisation to MXFP4 for the QFA_PV_FP4 contrast case (below): the Q/K
+ * block rule (E2M1 elements, E8M0 scale 2^(ceil(log2 amax) - 2)) applied to
+ * each (32 consecutive tokens, channel) block, token 2k in the low nibble of
+ * byte k; tokens past S count as 0.  FP4 tutorial, section "Direct-P" (P and
+ * V in MXFP4, one E8M0 scale per 32).
+ *   v      bf16 [B][H][S][D]
+ *   codes  out [B][H][ceil(S/32)][D][16], scales out [B][H][ceil(S/32)][D].
+ */
+qfa_status qfa_quantize_v4(const uint16_t* v, int B, int H, int S, int D, int block_size, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream);
+
+/*
  * Prefill forward (MpFA abstract; online softmax per the FP4 tutorial's
  * section "注意力慢在哪儿").  Q must be quantised with prescale
  * qfa_exp2_scale(softmax_scale), so s_j = q4 . k4_j is the logit of key j in
@@ -178,8 +190,7 @@ typedef enum qfa_pv_format { QFA_PV_FP8 = 0, QFA_PV_FP8_BLOCKP = 1, QFA_PV_FP4 =
  * qfa_fwd_prefill and qfa_fwd_decode with the P/V format as an argument; the
  * plain entry points are pv_format = QFA_PV_FP8.  For QFA_PV_FP4, v8 and v8s
  * carry the MXFP4 V of qfa_quantize_v4.  An unknown format gives
- * QFA_ERR_INVALID_ARG, a known one this library does not run
- * QFA_ERR_UNSUPPORTED.  Everything else is as for the plain entry points.
+ * QFA_ERR_INVALID_ARG.  Everything else is as for the plain entry points.
  */
 qfa_status qfa_fwd_prefill_ex(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
                               const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,

@@ -136,6 +136,11 @@ def test_pv_format_validation():
         fmt, ctypes.byref(ns), fake, ctypes.c_size_t(ws), fake, None, None)
     assert dec(5) == qfa.QFA_ERR_INVALID_ARG
     assert dec(qfa.QFA_PV_FP8_BLOCKP) == qfa.QFA_ERR_WORKSPACE          # workspace too small, as before
+    assert dec(qfa.QFA_PV_FP4) == qfa.QFA_ERR_WORKSPACE
+    # the MXFP4 V quantiser validates like the E4M3 one
+    assert _call_raw("qfa_quantize_v4", fake, 1, 1, 1, 64, 16, fake, fake, None) == qfa.QFA_ERR_UNSUPPORTED
+    assert _call_raw("qfa_quantize_v4", P(4097), 1, 1, 1, 64, 32, fake, fake, None) == qfa.QFA_ERR_INVALID_ARG
+    assert _call_raw("qfa_quantize_v4", None, 0, 1, 1, 64, 32, None, None, None) == qfa.QFA_OK
     # the plain entry points are the method's format
     assert _call_raw("qfa_fwd_prefill", fake, fake, fake, fake, None, None, fake, fake, 1, 4, 3, 8, 8, 128, 1,
                      F(0.125), 32, fake, None, None) == qfa.QFA_ERR_INVALID_ARG

@@ -280,12 +280,19 @@ BLOCKP_CASES = [
 ]
 
 
+@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8_BLOCKP, qfa.QFA_PV_FP4], ids=["blockp", "fp4"])
 @pytest.mark.parametrize("case", BLOCKP_CASES, ids=[c[-1] for c in BLOCKP_CASES])
-def test_prefill_blockp_small_all_rows(case):
+def test_prefill_pv_formats_small_all_rows(case, pv):
     B, Hq, Hkv, Sq, Skv, D, causal, smooth, koff, label = case
     q, k, v = _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed=zlib.crc32(label.encode()) % 1000, k_offset=koff, q_scale=2.0)
-    _check_prefill(q, k, v, causal, 1.0 / math.sqrt(D), smooth, _all_rows(B, Hq, Sq), label, fused=True,
-                   pv=qfa.QFA_PV_FP8_BLOCKP)
+    _check_prefill(q, k, v, causal, 1.0 / math.sqrt(D), smooth, _all_rows(B, Hq, Sq), label, fused=True, pv=pv)
+
+
+def test_prefill_fp4_two_pass_q_and_sq_gt_skv():
+    """QK4PV4 with Q quantised by the separate pass, and rows with no visible key."""
+    q, k, v = _rand_inputs(1, 4, 2, 300, 200, 128, seed=31, q_scale=2.0)
+    _check_prefill(q, k, v, True, 1.0 / math.sqrt(128), False, _all_rows(1, 4, 300), "fp4-sq>skv",
+                   pv=qfa.QFA_PV_FP4)
 
 
 def _spread_inputs(seed, Sq=128, Skv=1000, D=128):
@@ -313,7 +320,7 @@ def test_prefill_blockp_differs_where_blocks_spread():
     assert d > 0
 
 
-@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8, qfa.QFA_PV_FP8_BLOCKP])
+@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8, qfa.QFA_PV_FP8_BLOCKP, qfa.QFA_PV_FP4])
 def test_prefill_extreme_logits_far_and_rebase(pv):
     """Logits far beyond 100 in log2 units (the kernel's subtract-first path)
     and a row max that climbs by more than 64 binades across the key range
@@ -325,7 +332,7 @@ def test_prefill_extreme_logits_far_and_rebase(pv):
                    pv=pv)
 
 
-@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8, qfa.QFA_PV_FP8_BLOCKP])
+@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8, qfa.QFA_PV_FP8_BLOCKP, qfa.QFA_PV_FP4])
 def test_decode_extreme_logits(pv):
     Skv, D = 1200, 128
     q, k, v = _rand_inputs(2, 8, 2, 1, Skv, D, seed=10, q_scale=30.0)
@@ -333,7 +340,13 @@ def test_decode_extreme_logits(pv):
     _check_decode(q, k, v, 3, kv_lens=[1200, 700], label="decode-extreme", pv=pv)
 
 
+@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8_BLOCKP, qfa.QFA_PV_FP4], ids=["blockp", "fp4"])
 @pytest.mark.parametrize("smooth", [False, True])
-def test_decode_blockp(smooth):
+def test_decode_pv_formats(smooth, pv):
     q, k, v = _rand_inputs(3, 8, 2, 1, 1000, 128, seed=23, q_scale=2.0, k_offset=3.0 if smooth else 0.0)
-    _check_decode(q, k, v, 3, kv_lens=[1000, 517, 0], label="decode-blockp", smooth=smooth, pv=qfa.QFA_PV_FP8_BLOCKP)
+    _check_decode(q, k, v, 3, kv_lens=[1000, 517, 0], label="decode-pv%d" % pv, smooth=smooth, pv=pv)
+
+
+def test_decode_fp4_d64():
+    q, k, v = _rand_inputs(2, 4, 4, 1, 300, 64, seed=24)
+    _check_decode(q, k, v, 7, label="decode-fp4-d64", pv=qfa.QFA_PV_FP4)

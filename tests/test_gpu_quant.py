@@ -54,6 +54,24 @@ def test_v8_bitexact_shapes(shape):
     _check_v8(v.to(torch.bfloat16), "shape%s" % (shape,))
 
 
+def _check_v4(v: torch.Tensor, label: str):
+    say("quantize_v4", label, tuple(v.shape))
+    codes, scales = qfa.quantize_v4(v)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize_v4(bf16_bits(v))
+    assert np.array_equal(to_np(codes), oc), label + ": codes differ"
+    assert np.array_equal(to_np(scales), os_), label + ": scales differ"
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 75, 64), (2, 3, 1000, 128), (1, 1, 31, 128), (1, 1, 64, 256)])
+def test_v4_bitexact_shapes(shape):
+    g = torch.Generator(device="cuda").manual_seed(sum(shape) + 2)
+    v = torch.randn(shape, generator=g, device="cuda")
+    v[..., 5, :] *= 100.0
+    v[..., :, 7] *= 1e-3
+    _check_v4(v.to(torch.bfloat16), "shape%s" % (shape,))
+
+
 def test_quantizers_nonfinite_and_tiny():
     x = torch.randn((1, 1, 64, 128), device="cuda")
     x[0, 0, 1, 5] = float("nan")
@@ -64,6 +82,7 @@ def test_quantizers_nonfinite_and_tiny():
     _check_qk4(xb, False, "nonfinite")
     _check_qk4(xb, False, "nonfinite.prescaled", prescale=oracle.exp2_scale(0.125))
     _check_v8(xb, "nonfinite")
+    _check_v4(xb, "nonfinite")
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama16k", "qwen32k"])
