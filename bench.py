@@ -18,6 +18,11 @@ with HIP events on the stream it is launched on; its peak is the blended
 MXFP4 (Q K^T) / FP8 (P V) MFMA peak.  The CPU baseline is the oracle timed on
 a bounded sample of rows of the same workload on this host (about 15 s).
 
+The two P/V contrast formats (FP8 P with a scale per (row, 32 keys); MXFP4 P
+and V) are timed on the same workloads, kernels only, and reported under
+"variants" with their own roofline fractions (the MXFP4 prefill against the
+all-MXFP4 MFMA peak, the MXFP4 decode against the smaller cache).
+
 `--only prefill|decode` runs just that half (for hardware-counter passes);
 `--only copy` runs a plain device-to-device copy of 1 GiB, the reference
 kernel of known size that scales the FETCH_SIZE / WRITE_SIZE counters into
@@ -42,6 +47,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-variants", action="store_true")
     p.add_argument("--workload", default="llama16k")
     p.add_argument("--only", default="all", choices=("all", "prefill", "decode", "copy"))
     return p.parse_args()
@@ -177,9 +183,34 @@ def main():
                        "step": "quantize K (MXFP4) + V (FP8), then the prefill kernel with Q quantised in-kernel"},
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 2), "unit": "TFLOP/s",
                          "frac": round(achieved / peak, 4), "traffic": traffic,
-                         "kernel": "qfa::k_prefill<128,%s>" % ("true" if w.smooth else "false"),
+                         "kernel": "qfa::k_prefill<128,%s,0>" % ("true" if w.smooth else "false"),
                          "kernel_ms": round(kern_ms, 4), "algorithmic_flop_per_launch": flops + comp},
         })
+        if not args.no_variants and args.only == "all":
+            out["variants"] = {}
+            for name, pv in (("qk4pv8_blockp", qfa.QFA_PV_FP8_BLOCKP), ("qk4pv4", qfa.QFA_PV_FP4)):
+                fp4 = pv == qfa.QFA_PV_FP4
+                vq, vqs = qfa.quantize_v4(v) if fp4 else qfa.quantize_v8(v)
+                qfa.qfa_quantize_qk4(k, B, Hkv, S, D, 32, int(w.smooth), 1.0, k4, k4s, kbar, stream)
+                vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.steps)]
+                for i in range(args.warmup + args.steps):
+                    j = i - args.warmup
+                    if j >= 0:
+                        vev[j][0].record(stream)
+                    qfa.qfa_fwd_prefill_ex(None, None, k4, k4s, kbar, q, vq, vqs, B, Hq, Hkv, S, S, D,
+                                           int(w.causal), w.scale, 32, pv, O, lse, stream)
+                    if j >= 0:
+                        vev[j][1].record(stream)
+                torch.cuda.synchronize()
+                vk = float(np.mean([a.elapsed_time(b) for a, b in vev]))
+                vach = (flops + comp) / (vk * 1e-3) / 1e12
+                vpeak = rl.blended_peak(flops, comp, pv_fp4=fp4) / 1e12
+                out["variants"][name] = {
+                    "prefill": {"kernel_ms": round(vk, 4), "achieved": round(vach, 2), "peak": round(vpeak, 2),
+                                "unit": "TFLOP/s", "frac": round(vach / vpeak, 4),
+                                "kernel": "qfa::k_prefill<128,%s,%d>" % ("true" if w.smooth else "false", pv)}}
+                del vq, vqs
         del O, lse
     # ------------------------------------------------------------------ decode half
     if args.only in ("all", "decode") and not args.no_decode:
@@ -227,9 +258,33 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": rl.PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": round(gbs * 1e9 / rl.PEAK_HBM, 4),
                          "traffic": traffic_from_profile("decode_b64_traffic.json", src),
-                         "kernel": "qfa::k_decode_split<128,false> + k_decode_merge<128>",
+                         "kernel": "qfa::k_decode_split<128,false,0> + k_decode_merge<128>",
                          "algorithmic_bytes_per_launch": dbytes},
         }
+        if not args.no_variants and args.only == "all":
+            vd = make_inputs(wd, seed=0, device=dev)["v"]
+            for name, pv in (("qk4pv8_blockp", qfa.QFA_PV_FP8_BLOCKP), ("qk4pv4", qfa.QFA_PV_FP4)):
+                fp4 = pv == qfa.QFA_PV_FP4
+                del v8d, v8sd
+                v8d, v8sd = qfa.quantize_v4(vd) if fp4 else qfa.quantize_v8(vd)
+                vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.steps)]
+                for i in range(args.warmup + args.steps):
+                    j = i - args.warmup
+                    if j >= 0:
+                        vev[j][0].record(stream)
+                    qfa.qfa_fwd_decode_ex(None, None, k4d, k4sd, None, qd, v8d, v8sd, Bd, Hqd, Hkvd, L, None, Dd,
+                                          wd.scale, 32, pv, splits, ws, wsb, Od, lsed, stream)
+                    if j >= 0:
+                        vev[j][1].record(stream)
+                torch.cuda.synchronize()
+                vk = float(np.mean([a.elapsed_time(b) for a, b in vev]))
+                vb = rl.decode_algorithmic_bytes(Bd, Hqd, Hkvd, L, Dd, v_fp4=fp4)
+                vg = vb / (vk * 1e-3) / 1e9
+                out.setdefault("variants", {}).setdefault(name, {})["decode"] = {
+                    "kernel_ms": round(vk, 4), "achieved": round(vg, 1), "peak": rl.PEAK_HBM / 1e9, "unit": "GB/s",
+                    "frac": round(vg * 1e9 / rl.PEAK_HBM, 4), "algorithmic_bytes_per_launch": vb}
+            del vd
         del k4d, v8d, ws
     # ------------------------------------------------------------------ CPU baseline (oracle)
     if args.only in ("all", "prefill") and not args.no_cpu_baseline:

@@ -27,18 +27,21 @@ def kv_cache_bytes(layers: int, kv_heads: int, head_dim: int, seq_len: int, byte
     return int(2 * layers * kv_heads * head_dim * seq_len * bytes_per_element * batch)
 
 
-def decode_algorithmic_bytes(B: int, Hq: int, Hkv: int, L: int, D: int, include_q_o: bool = True) -> int:
-    per_tok = D // 2 + D // 32 + D + D // 32
+def decode_algorithmic_bytes(B: int, Hq: int, Hkv: int, L: int, D: int, include_q_o: bool = True,
+                             v_fp4: bool = False) -> int:
+    """v_fp4: V held in MXFP4 (D/2 bytes of codes per token) instead of E4M3."""
+    per_tok = D // 2 + D // 32 + (D // 2 if v_fp4 else D) + D // 32
     total = B * Hkv * L * per_tok
     if include_q_o:
         total += B * Hq * D * 2 + B * Hq * D * 4
     return total
 
 
-def prefill_roof_seconds(flops_qkpv: float, comp_flops: float = 0.0) -> float:
+def prefill_roof_seconds(flops_qkpv: float, comp_flops: float = 0.0, pv_fp4: bool = False) -> float:
+    """pv_fp4: P V also on the MXFP4 MFMA (the full-FP4 contrast case)."""
     half = flops_qkpv / 2.0
-    return half / PEAK_FP4 + half / PEAK_FP8 + comp_flops / PEAK_BF16
+    return half / PEAK_FP4 + half / (PEAK_FP4 if pv_fp4 else PEAK_FP8) + comp_flops / PEAK_BF16
 
 
-def blended_peak(flops_qkpv: float, comp_flops: float = 0.0) -> float:
-    return (flops_qkpv + comp_flops) / prefill_roof_seconds(flops_qkpv, comp_flops)
+def blended_peak(flops_qkpv: float, comp_flops: float = 0.0, pv_fp4: bool = False) -> float:
+    return (flops_qkpv + comp_flops) / prefill_roof_seconds(flops_qkpv, comp_flops, pv_fp4)
