@@ -21,6 +21,7 @@ attention) are "parity unpinned": the pages print no operator-level figure.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from typing import Optional, Sequence
@@ -87,6 +88,10 @@ def lib():
         L.orc_dequant_qk4.argtypes = [P, P, I64, I64, P]
         L.orc_dequant_v8.restype = None
         L.orc_dequant_v8.argtypes = [P, P, I64, I64, P]
+        L.orc_quantize_nvfp4.restype = None
+        L.orc_quantize_nvfp4.argtypes = [P, I64, I64, I64, I64, I, F, F, P, P, P]
+        L.orc_dequant_nvfp4.restype = None
+        L.orc_dequant_nvfp4.argtypes = [P, P, I64, I64, D, P]
         L.orc_quantize_v4.restype = None
         L.orc_quantize_v4.argtypes = [P, I64, I64, I64, I64, P, P]
         L.orc_dequant_v4.restype = None
@@ -197,6 +202,43 @@ def quantize_qk4(x_bits: np.ndarray, smooth: bool = False, prescale: float = 1.0
     lib().orc_quantize_qk4(_p(x), B, H, S, D, int(bool(smooth)), float(np.float32(prescale)), _p(codes),
                            _p(scales), _p(kbar))
     return codes, scales, kbar
+
+
+def nvfp4_tensor_scale(amax: float) -> float:
+    """Per-tensor NVFP4 scale as a power of two: the smallest 2^k with
+    amax / (6 * 2^k) <= 448 (E2M1 max 6, E4M3 max 448); 1 for an all-zero tensor."""
+    if not (amax > 0.0) or not math.isfinite(amax):
+        return 1.0
+    k = math.ceil(math.log2(amax / (6.0 * 448.0)))
+    while amax / (6.0 * 2.0**k) > 448.0:
+        k += 1
+    while k > -126 and amax / (6.0 * 2.0**(k - 1)) <= 448.0:
+        k -= 1
+    return 2.0**k
+
+
+def quantize_nvfp4(x_bits: np.ndarray, g: float, smooth: bool = False, prescale: float = 1.0):
+    """x [B,H,S,D] bf16 bits -> NVFP4 (codes [B,H,S,D/2] u8, E4M3 scales [B,H,S,D/16] u8,
+    kbar or None) with per-tensor scale g (a power of two)."""
+    x = _c(x_bits, np.uint16)
+    B, H, S, D = x.shape
+    codes = np.empty((B, H, S, D // 2), np.uint8)
+    scales = np.empty((B, H, S, D // 16), np.uint8)
+    nt = (S + TILE - 1) // TILE
+    kbar = np.empty((B, H, nt, D), np.uint16) if smooth else None
+    lib().orc_quantize_nvfp4(_p(x), B, H, S, D, int(bool(smooth)), float(np.float32(prescale)), float(g), _p(codes),
+                             _p(scales), _p(kbar))
+    return codes, scales, kbar
+
+
+def dequant_nvfp4(codes: np.ndarray, scales: np.ndarray, g: float) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    D = codes.shape[-1] * 2
+    rows = codes.size // (D // 2)
+    out = np.empty(codes.shape[:-1] + (D,), np.float64)
+    lib().orc_dequant_nvfp4(_p(codes), _p(scales), rows, D, float(g), _p(out))
+    return out
 
 
 def quantize_v8(v_bits: np.ndarray):
@@ -312,13 +354,14 @@ def _rows_by_group(rows: np.ndarray, Hq: int, Hkv: int):
 
 
 def prefill_rows(q_bits, k_bits, v_bits, rows: Sequence, causal: bool, softmax_scale: float,
-                 smooth: bool = False, exact: bool = True, pv: int = PV_FP8):
+                 smooth: bool = False, exact: bool = True, pv: int = PV_FP8, nvfp4=None):
     """Quantise Q/K/V with the oracle's quantizers and evaluate the listed rows.
 
     q_bits [B,Hq,Sq,D], k_bits/v_bits [B,Hkv,Skv,D] (bf16 bit patterns, uint16).
     rows: array [n,3] of (b, h, i).  Returns dict with O_q, lse_q (method) and,
     if exact, O_x, lse_x (exact FP64 attention on the bf16 inputs).  pv picks
-    the P/V format: PV_FP8 (the method), PV_FP8_BLOCKP or PV_FP4.
+    the P/V format: PV_FP8 (the method), PV_FP8_BLOCKP or PV_FP4.  nvfp4 =
+    (g_q, g_k): Q and K in NVFP4 with those per-tensor scales instead of MXFP4.
     """
     rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
     B, Hq, Sq, D = q_bits.shape
@@ -334,8 +377,12 @@ def prefill_rows(q_bits, k_bits, v_bits, rows: Sequence, causal: bool, softmax_s
         r = rows[idx]
         kq = np.ascontiguousarray(k_bits[b:b + 1, g:g + 1])
         vq = np.ascontiguousarray(v_bits[b:b + 1, g:g + 1])
-        kc, ks, kb = quantize_qk4(kq, smooth=smooth)
-        Kd = dequant_qk4(kc, ks)[0, 0]
+        if nvfp4 is None:
+            kc, ks, kb = quantize_qk4(kq, smooth=smooth)
+            Kd = dequant_qk4(kc, ks)[0, 0]
+        else:
+            kc, ks, kb = quantize_nvfp4(kq, nvfp4[1], smooth=smooth)
+            Kd = dequant_nvfp4(kc, ks, nvfp4[1])[0, 0]
         Vd = _quant_dequant_v(vq, Skv, pv)
         Kbar = bf16_to_f64(kb[0, 0]) if smooth else None
         # query rows: quantise each needed (b, h) head once
@@ -344,8 +391,12 @@ def prefill_rows(q_bits, k_bits, v_bits, rows: Sequence, causal: bool, softmax_s
         for h in np.unique(r[:, 1]):
             sel = np.nonzero(r[:, 1] == h)[0]
             qh = np.ascontiguousarray(q_bits[b:b + 1, h:h + 1])
-            qc_, qs_, _ = quantize_qk4(qh, prescale=exp2_scale(softmax_scale))
-            qd = dequant_qk4(qc_, qs_)[0, 0]
+            if nvfp4 is None:
+                qc_, qs_, _ = quantize_qk4(qh, prescale=exp2_scale(softmax_scale))
+                qd = dequant_qk4(qc_, qs_)[0, 0]
+            else:
+                qc_, qs_, _ = quantize_nvfp4(qh, nvfp4[0], prescale=exp2_scale(softmax_scale))
+                qd = dequant_nvfp4(qc_, qs_, nvfp4[0])[0, 0]
             Qd[sel] = qd[r[sel, 2]]
             Qc[sel] = bf16_to_f64(q_bits[b, h][r[sel, 2]])
         O, lse = attn_quant_rows(Qd, r[:, 2], Kd, Vd, Sq, causal, softmax_scale,
@@ -362,7 +413,7 @@ def prefill_rows(q_bits, k_bits, v_bits, rows: Sequence, causal: bool, softmax_s
 
 
 def decode_rows(q_bits, k_bits, v_bits, rows: Sequence, softmax_scale: float, num_splits: int,
-                kv_lens: Optional[Sequence[int]] = None, exact: bool = True, pv: int = PV_FP8):
+                kv_lens: Optional[Sequence[int]] = None, exact: bool = True, pv: int = PV_FP8, nvfp4=None):
     """Decode (one query token per sequence) with the split-KV schedule.
 
     q_bits [B,Hq,1,D]; k_bits/v_bits [B,Hkv,Smax,D].  rows [n,3] of (b, h, 0).
@@ -385,14 +436,22 @@ def decode_rows(q_bits, k_bits, v_bits, rows: Sequence, softmax_scale: float, nu
         per = max(1, -(-nt // max(1, num_splits)))
         kq = np.ascontiguousarray(k_bits[b:b + 1, g:g + 1, :L])
         vq = np.ascontiguousarray(v_bits[b:b + 1, g:g + 1, :L])
-        kc, ks, _ = quantize_qk4(kq)
-        Kd = dequant_qk4(kc, ks)[0, 0]
+        if nvfp4 is None:
+            kc, ks, _ = quantize_qk4(kq)
+            Kd = dequant_qk4(kc, ks)[0, 0]
+        else:
+            kc, ks, _ = quantize_nvfp4(kq, nvfp4[1])
+            Kd = dequant_nvfp4(kc, ks, nvfp4[1])[0, 0]
         Vd = _quant_dequant_v(vq, L, pv)
         Qd = np.zeros((len(idx), D))
         for j, (bb, h, _) in enumerate(r):
-            qc_, qs_, _ = quantize_qk4(np.ascontiguousarray(q_bits[bb:bb + 1, h:h + 1]),
-                                       prescale=exp2_scale(softmax_scale))
-            Qd[j] = dequant_qk4(qc_, qs_)[0, 0, 0]
+            qh = np.ascontiguousarray(q_bits[bb:bb + 1, h:h + 1])
+            if nvfp4 is None:
+                qc_, qs_, _ = quantize_qk4(qh, prescale=exp2_scale(softmax_scale))
+                Qd[j] = dequant_qk4(qc_, qs_)[0, 0, 0]
+            else:
+                qc_, qs_, _ = quantize_nvfp4(qh, nvfp4[0], prescale=exp2_scale(softmax_scale))
+                Qd[j] = dequant_nvfp4(qc_, qs_, nvfp4[0])[0, 0, 0]
         O, lse = attn_quant_rows(Qd, np.zeros(len(idx), np.int64), Kd, Vd, 1, False, softmax_scale,
                                  split_tiles=per, p_mode=_P_MODE_OF_PV[pv])
         out["O_q"][idx] = O

@@ -332,6 +332,69 @@ void orc_quantize_v4(const uint16_t* v, int64_t B, int64_t H, int64_t S, int64_t
   }
 }
 
+/* NVFP4 quantisation of one run of 16 elements given as binary32 values, with
+ * the per-tensor scale g (a power of two): the block scale is the E4M3 code
+ * (RNE, saturating at 448) of the binary32 quotient fl32(fl32(amax / g) / 6),
+ * 6 being the largest E2M1 magnitude; each element is the E2M1 code (RNE,
+ * saturating at 6) of the binary32 quotient fl32(x / (s g)) with s the
+ * decoded scale.  A scale of 0 gives zero codes; a block holding a NaN or an
+ * infinity gets scale code 0x7F and zero codes.  Writes 8 code bytes (even
+ * element in the low nibble) and returns the scale code.  [FA4tut] "FP4 只有约
+ * 15 个可表示的数" (NVFP4: blocks of 16, E4M3 scale, optional FP32 tensor
+ * scale; about 4.5 bits per value) and [MpFA] abstract (NVFP4 for QK). */
+static int nvfp4_block(const float* x, float g, uint8_t* codes) {
+  float amax = 0.0f;
+  int finite = 1;
+  for (int i = 0; i < 16; ++i) {
+    if (!isfinite(x[i])) finite = 0;
+    else if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+  }
+  memset(codes, 0, 8);
+  if (!finite) return 0x7F;
+  volatile float q = amax / g; /* exact: g is a power of two */
+  q = q / 6.0f;                /* binary32, correctly rounded */
+  int sc = orc_e4m3_encode((double)q);
+  float t = (float)orc_e4m3_value(sc) * g; /* exact */
+  if (t == 0.0f) return sc;
+  for (int i = 0; i < 16; i += 2) {
+    volatile float a = x[i] / t, b = x[i + 1] / t;
+    int lo = orc_e2m1_encode((double)a);
+    int hi = orc_e2m1_encode((double)b);
+    codes[i / 2] = (uint8_t)(lo | (hi << 4));
+  }
+  return sc;
+}
+
+/* Q or K [B][H][S][D] bf16 -> NVFP4 codes [B][H][S][D/2] and E4M3 block scales
+ * [B][H][S][D/16], with the per-tensor scale g (a power of two).  smooth and
+ * prescale as for orc_quantize_qk4: the quantised value is fl32(fl32(K - Kbar)
+ * * prescale). */
+void orc_quantize_nvfp4(const uint16_t* x, int64_t B, int64_t H, int64_t S, int64_t D, int smooth, float prescale,
+                        float g, uint8_t* codes, uint8_t* scales, uint16_t* kbar) {
+  int64_t nt = (S + QFA_ORC_TILE - 1) / QFA_ORC_TILE;
+  int64_t nb = D / 16;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    const uint16_t* xs = x + bh * S * D;
+    uint16_t* kb = smooth ? kbar + bh * nt * D : NULL;
+    if (smooth) kbar_of(xs, S, D, kb);
+    float buf[16];
+    for (int64_t s = 0; s < S; ++s) {
+      for (int64_t blk = 0; blk < nb; ++blk) {
+        for (int i = 0; i < 16; ++i) {
+          int64_t c = blk * 16 + i;
+          double v = orc_bf16_value(xs[s * D + c]);
+          if (smooth) v = (double)(float)(v - orc_bf16_value(kb[(s / QFA_ORC_TILE) * D + c]));
+          if (prescale != 1.0f) v = (double)((float)v * prescale);
+          buf[i] = (float)v;
+        }
+        int64_t row = bh * S + s;
+        scales[row * nb + blk] = (uint8_t)nvfp4_block(buf, g, codes + row * (D / 2) + blk * 8);
+      }
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------- */
 /* Dequantizers (exact in binary64)                                          */
 /* ------------------------------------------------------------------------- */
@@ -344,6 +407,17 @@ void orc_dequant_qk4(const uint8_t* codes, const uint8_t* scales, int64_t rows, 
       uint8_t byte = codes[r * (D / 2) + c / 2];
       int code = (c & 1) ? (byte >> 4) : (byte & 15);
       out[r * D + c] = orc_e2m1_value(code) * orc_e8m0_value(scales[r * nb + c / QFA_ORC_BLOCK]);
+    }
+}
+
+/* NVFP4 rows: codes [rows][D/2], E4M3 scales [rows][D/16], tensor scale g -> v * s * g. */
+void orc_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t D, double g, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < D; ++c) {
+      uint8_t byte = codes[r * (D / 2) + c / 2];
+      int code = (c & 1) ? (byte >> 4) : (byte & 15);
+      out[r * D + c] = orc_e2m1_value(code) * orc_e4m3_value(scales[r * (D / 16) + c / 16]) * g;
     }
 }
 

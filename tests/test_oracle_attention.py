@@ -475,3 +475,32 @@ def test_pv_variants_close_to_exact_attention(pv):
     d0 = oracle.decode_rows(q[:, :, :1], k, v, np.array([(0, 0, 0), (0, 1, 0)]), 0.125, 2)
     d1 = oracle.decode_rows(q[:, :, :1], k, v, np.array([(0, 0, 0), (0, 1, 0)]), 0.125, 2, pv=pv)
     assert rel(d1) < 2.5 * rel(d0) + 1e-12
+
+
+def test_nvfp4_qk_more_accurate_than_mxfp4():
+    """Q and K in NVFP4 (blocks of 16 with E4M3 scales) run through the same
+    online-softmax schedule; with twice as many, finer scales the result is
+    closer to exact attention than with MXFP4 ([FA4tut] "FP4 只有约 15 个可表示的数":
+    NVFP4 matches local dynamic range more often)."""
+    rng = np.random.default_rng(61)
+    B, Hq, Hkv, S, D = 1, 2, 1, 200, 64
+
+    def bf(x):
+        return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q = bf(rng.standard_normal((B, Hq, S, D)))
+    k = bf(rng.standard_normal((B, Hkv, S, D)))
+    v = bf(rng.standard_normal((B, Hkv, S, D)))
+    rows = np.array([(0, h, i) for h in range(Hq) for i in range(0, S, 7)])
+    c2 = oracle.exp2_scale(0.125)
+    gq = oracle.nvfp4_tensor_scale(float(np.abs(oracle.bf16_to_f64(q) * np.float32(c2)).max()))
+    gk = oracle.nvfp4_tensor_scale(float(np.abs(oracle.bf16_to_f64(k)).max()))
+
+    def rel(r):
+        return np.linalg.norm(r["O_q"] - r["O_x"]) / np.linalg.norm(r["O_x"])
+    r0 = oracle.prefill_rows(q, k, v, rows, True, 0.125)
+    r1 = oracle.prefill_rows(q, k, v, rows, True, 0.125, nvfp4=(gq, gk))
+    assert rel(r1) < 0.8 * rel(r0)
+    # a doubled tensor scale halves every block scale: where the halved scale
+    # stays an E4M3 normal the decoded values are the same, so O is (almost) too
+    r2 = oracle.prefill_rows(q, k, v, rows, True, 0.125, nvfp4=(gq, gk * 2))
+    assert np.abs(r2["O_q"] - r1["O_q"]).max() < 1e-3

@@ -313,3 +313,70 @@ def test_v4_quantizer_bruteforce_vs_printed_table():
                 code = (byte >> 4) if j % 2 else (byte & 15)
                 mag = table[code & 7] * 2.0 ** (int(scales[0, h, blk, c]) - 127)
                 assert dq[j, c] == (-mag if code & 8 else mag)
+
+
+def test_nvfp4_tensor_scale_closed_forms():
+    """The per-tensor scale is the smallest power of two g with amax / (6 g) <= 448."""
+    assert oracle.nvfp4_tensor_scale(6 * 448.0) == 1.0
+    assert oracle.nvfp4_tensor_scale(6 * 448.0 * 1.0001) == 2.0
+    assert oracle.nvfp4_tensor_scale(6 * 448.0 / 2) == 0.5
+    assert oracle.nvfp4_tensor_scale(0.0) == 1.0
+    for amax in (1e-3, 0.37, 5.0, 1234.5, 1e6):
+        g = oracle.nvfp4_tensor_scale(amax)
+        assert amax / (6 * g) <= 448.0 < amax / (6 * g / 2)
+        assert math.frexp(g)[0] == 0.5
+
+
+def test_nvfp4_quantizer_bruteforce():
+    """NVFP4 blocks of 16: the E4M3 scale (torch float8 of the binary32 quotient
+    fl32(fl32(amax / g) / 6)) and the E2M1 elements (nearest-even over the
+    printed magnitudes of the binary32 quotient x / (s g)), brute-forced; and
+    the format's 4.5 bits per element."""
+    table = gold("e2m1_magnitudes.json")["magnitudes"]
+    g_bits = gold("mx_bits_per_element.json")
+    assert 4 + 8 / 16 == g_bits["nvfp4_block16_bits"]
+    rng = np.random.default_rng(19)
+    B, H, S, D = 1, 2, 23, 64
+    x = rng.standard_normal((B, H, S, D)).astype(np.float32)
+    x[0, 0, 3, 5] *= 300.0              # outlier: sets the tensor scale
+    x[0, 1, 4, :16] = 0.0               # all-zero block
+    x[0, 1, 5, 16:32] *= 1e-4           # small block, small scale
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xv = oracle.bf16_to_f64(bits).astype(np.float32)
+    for prescale in (1.0, oracle.exp2_scale(0.125)):
+        xp = xv * np.float32(prescale) if prescale != 1.0 else xv
+        g = oracle.nvfp4_tensor_scale(float(np.abs(xp).max()))
+        codes, scales, _ = oracle.quantize_nvfp4(bits, g, prescale=prescale)
+        assert codes.shape == (B, H, S, D // 2) and scales.shape == (B, H, S, D // 16)
+        for h in range(H):
+            for s in range(S):
+                for blk in range(D // 16):
+                    v = xp[0, h, s, blk * 16:(blk + 1) * 16]
+                    q = np.float32(np.float32(np.abs(v).max()) / np.float32(g)) / np.float32(6.0)
+                    want_sc = torch.tensor([float(q)], dtype=torch.float32).to(torch.float8_e4m3fn)
+                    want_sc = int(want_sc.view(torch.uint8).item())
+                    assert scales[0, h, s, blk] == want_sc, (prescale, h, s, blk)
+                    t = np.float32(oracle.e4m3_value(want_sc)) * np.float32(g)
+                    for i in range(16):
+                        if t == 0:
+                            want = 0
+                        else:
+                            a = float(np.float32(v[i]) / t)
+                            want = (8 if math.copysign(1.0, a) < 0 else 0) | _nearest_even_bruteforce(abs(a), table)
+                        byte = codes[0, h, s, (blk * 16 + i) // 2]
+                        got = (byte >> 4) if i % 2 else (byte & 15)
+                        assert got == want, (prescale, h, s, blk, i)
+        assert (scales[0, 1, 4, 0] == 0) and (codes[0, 1, 4, :8] == 0).all()
+        deq = oracle.dequant_nvfp4(codes, scales, g)
+        # decoding is code value x block scale x tensor scale
+        c0 = codes[0, 0, 0, 0] & 15
+        assert deq[0, 0, 0, 0] == (-1 if c0 & 8 else 1) * table[c0 & 7] * oracle.e4m3_value(scales[0, 0, 0, 0]) * g
+
+
+def test_nvfp4_nonfinite_block():
+    x = np.ones((1, 1, 1, 32), np.float32)
+    x[0, 0, 0, 20] = np.nan
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    codes, scales, _ = oracle.quantize_nvfp4(bits, 1.0)
+    assert scales[0, 0, 0, 1] == 0x7F and (codes[0, 0, 0, 8:] == 0).all()
+    assert scales[0, 0, 0, 0] != 0x7F
