@@ -12,6 +12,7 @@ the ``qfa_*`` functions.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional
 
@@ -36,6 +37,7 @@ EXPORTS = (
     "qfa_quantize_qk4", "qfa_quantize_v8", "qfa_fwd_prefill", "qfa_fwd_decode",
     "qfa_decode_workspace_bytes", "qfa_decode_default_splits", "qfa_exp2_scale", "qfa_kv_append",
     "qfa_fwd_prefill_ex", "qfa_fwd_decode_ex", "qfa_quantize_v4",
+    "qfa_quantize_nvfp4", "qfa_fwd_prefill_nvfp4", "qfa_fwd_decode_nvfp4",
     "qfa_status_string", "qfa_version",
 )
 
@@ -60,6 +62,13 @@ def lib() -> ctypes.CDLL:
         L.qfa_quantize_qk4.argtypes = [P, I, I, I, I, I, I, F, P, P, P, P]
         L.qfa_quantize_v8.restype = I
         L.qfa_quantize_v8.argtypes = [P, I, I, I, I, I, P, P, P]
+        L.qfa_quantize_nvfp4.restype = I
+        L.qfa_quantize_nvfp4.argtypes = [P, I, I, I, I, I, I, F, F, P, P, P, P]
+        L.qfa_fwd_prefill_nvfp4.restype = I
+        L.qfa_fwd_prefill_nvfp4.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, F, F, P, P, P]
+        L.qfa_fwd_decode_nvfp4.restype = I
+        L.qfa_fwd_decode_nvfp4.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P, I, F, F, F, ctypes.POINTER(I), P,
+                                           SZ, P, P, P]
         L.qfa_quantize_v4.restype = I
         L.qfa_quantize_v4.argtypes = [P, I, I, I, I, I, P, P, P]
         L.qfa_fwd_prefill.restype = I
@@ -141,6 +150,34 @@ def qfa_quantize_qk4(x, B, H, S, D, block_size, smooth, prescale, codes, scales,
 def qfa_quantize_v8(v, B, H, S, D, block_size, codes, scales, stream=None):
     _check("qfa_quantize_v8", lib().qfa_quantize_v8(_ptr(_u16(v)), B, H, S, D, block_size, _ptr(codes),
                                                     _ptr(scales), _stream(stream)))
+
+
+def qfa_quantize_nvfp4(x, B, H, S, D, block_size, smooth, prescale, tensor_scale, codes, scales, kbar,
+                       stream=None):
+    _check("qfa_quantize_nvfp4", lib().qfa_quantize_nvfp4(
+        _ptr(_u16(x)), B, H, S, D, block_size, int(smooth), float(prescale), float(tensor_scale), _ptr(codes),
+        _ptr(scales), _ptr(None if kbar is None else _u16(kbar)), _stream(stream)))
+
+
+def qfa_fwd_prefill_nvfp4(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_q, S_kv, D, causal, softmax_scale,
+                          q_tensor_scale, k_tensor_scale, O, lse, stream=None):
+    _check("qfa_fwd_prefill_nvfp4", lib().qfa_fwd_prefill_nvfp4(
+        _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(None if kbar is None else _u16(kbar)),
+        _ptr(None if q_bf16 is None else _u16(q_bf16)), _ptr(v8), _ptr(v8s), B, Hq, Hkv, S_q, S_kv, D,
+        int(causal), float(softmax_scale), float(q_tensor_scale), float(k_tensor_scale), _ptr(O), _ptr(lse),
+        _stream(stream)))
+
+
+def qfa_fwd_decode_nvfp4(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D, softmax_scale,
+                         q_tensor_scale, k_tensor_scale, num_splits, workspace, workspace_bytes, O, lse,
+                         stream=None) -> int:
+    ns = ctypes.c_int(int(num_splits))
+    _check("qfa_fwd_decode_nvfp4", lib().qfa_fwd_decode_nvfp4(
+        _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(None if kbar is None else _u16(kbar)),
+        _ptr(None if q_bf16 is None else _u16(q_bf16)), _ptr(v8), _ptr(v8s), B, Hq, Hkv, S_kv_max,
+        _ptr(kv_lens), D, float(softmax_scale), float(q_tensor_scale), float(k_tensor_scale), ctypes.byref(ns),
+        _ptr(workspace), int(workspace_bytes), _ptr(O), _ptr(lse), _stream(stream)))
+    return ns.value
 
 
 def qfa_quantize_v4(v, B, H, S, D, block_size, codes, scales, stream=None):
@@ -235,6 +272,27 @@ def quantize_v8(v: torch.Tensor, stream=None):
     scales = torch.empty((B, H, nb, D), dtype=torch.uint8, device=v.device)
     qfa_quantize_v8(v, B, H, S, D, 32, codes, scales, stream)
     return codes, scales
+
+
+def nvfp4_tensor_scale(amax: float) -> float:
+    """Per-tensor NVFP4 scale: the smallest power of two g with amax / (6 g) <= 448
+    (1 for an all-zero or non-finite amax).  Host arithmetic only."""
+    amax = float(amax)
+    if not (amax > 0.0) or not math.isfinite(amax):
+        return 1.0
+    m, e = math.frexp(amax / (6.0 * 448.0))  # value = m * 2^e, m in [0.5, 1)
+    k = e - 1 if m == 0.5 else e             # smallest k with 2^k >= value
+    return math.ldexp(1.0, max(k, -126))
+
+
+def quantize_nvfp4(x: torch.Tensor, tensor_scale: float, smooth: bool = False, prescale: float = 1.0, stream=None):
+    """x bf16 [B,H,S,D] -> NVFP4 (codes u8 [B,H,S,D/2], E4M3 scales u8 [B,H,S,D/16], kbar or None)."""
+    B, H, S, D = x.shape
+    codes = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H, S, D // 16), dtype=torch.uint8, device=x.device)
+    kbar = torch.empty((B, H, (S + 127) // 128, D), dtype=torch.bfloat16, device=x.device) if smooth else None
+    qfa_quantize_nvfp4(x, B, H, S, D, 16, smooth, prescale, tensor_scale, codes, scales, kbar, stream)
+    return codes, scales, kbar
 
 
 def quantize_v4(v: torch.Tensor, stream=None):

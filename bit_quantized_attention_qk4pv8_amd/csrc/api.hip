@@ -69,6 +69,27 @@ qfa_status qfa_quantize_v8(const uint16_t* v, int B, int H, int S, int D, int bl
   return from_hip(qfa::launch_quant_v8(v, B, H, S, D, codes, scales, stream));
 }
 
+// a positive, finite power of two (the per-tensor NVFP4 scale)
+static bool pow2_ok(float g) {
+  if (!(g > 0.0f) || !isfinite(g)) return false;
+  int e;
+  return frexpf(g, &e) == 0.5f;
+}
+
+qfa_status qfa_quantize_nvfp4(const uint16_t* x, int B, int H, int S, int D, int block_size, int smooth,
+                              float prescale, float tensor_scale, uint8_t* codes, uint8_t* scales, uint16_t* kbar,
+                              hipStream_t stream) {
+  if (block_size != 16 || !qk_dim_ok(D)) return QFA_ERR_UNSUPPORTED;
+  if (B < 0 || H < 0 || S < 0 || (long long)B * H > 65535) return QFA_ERR_INVALID_ARG;
+  if (smooth != 0 && smooth != 1) return QFA_ERR_INVALID_ARG;
+  if ((smooth != 0) != (kbar != nullptr)) return QFA_ERR_INVALID_ARG;
+  if (!(prescale > 0.0f) || !isfinite(prescale) || !pow2_ok(tensor_scale)) return QFA_ERR_INVALID_ARG;
+  if ((long long)B * H * S == 0) return QFA_OK;
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return QFA_ERR_INVALID_ARG;
+  if (kbar && !aligned16(kbar)) return QFA_ERR_INVALID_ARG;
+  return from_hip(qfa::launch_quant_nvfp4(x, B, H, S, D, smooth, prescale, tensor_scale, codes, scales, kbar, stream));
+}
+
 qfa_status qfa_quantize_v4(const uint16_t* v, int B, int H, int S, int D, int block_size, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream) {
   if (block_size != 32 || !qk_dim_ok(D)) return QFA_ERR_UNSUPPORTED;
@@ -138,6 +159,34 @@ qfa_status qfa_fwd_prefill_ex(const uint8_t* q4, const uint8_t* q4s, const uint8
   return from_hip(qfa::launch_prefill(a, stream));
 }
 
+qfa_status qfa_fwd_prefill_nvfp4(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                                 const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                                 int B, int Hq, int Hkv, int S_q, int S_kv, int D, int causal, float softmax_scale,
+                                 float q_tensor_scale, float k_tensor_scale, float* O, float* lse, hipStream_t stream) {
+  if (S_q < 0 || S_kv < 0 || (causal != 0 && causal != 1)) return QFA_ERR_INVALID_ARG;
+  if (!pow2_ok(q_tensor_scale) || !pow2_ok(k_tensor_scale)) return QFA_ERR_INVALID_ARG;
+  if ((long long)B * Hq * S_q == 0) return QFA_OK;
+  if (!q4 || !q4s) return QFA_ERR_INVALID_ARG;  // NVFP4 Q comes quantised
+  qfa_status st = check_attn_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, D, softmax_scale, 32, O);
+  if (st != QFA_OK) return st;
+  const long long nq = (S_q + 31) / 32;
+  const int G = Hq / Hkv;
+  const long long nwg = (long long)B * Hkv * ((G + 7) / 8) * nq;
+  if (nwg > 0x7FFFFFFFLL) return QFA_ERR_INVALID_ARG;
+  qfa::AttnArgs a{};
+  a.q4 = q4; a.q4s = q4s; a.k4 = k4; a.k4s = k4s; a.v8 = v8; a.v8s = v8s;
+  a.kbar = kbar; a.qbf = q_bf16; a.kv_lens = nullptr;
+  a.O = O; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = S_q; a.Skv = S_kv; a.D = D; a.G = G;
+  a.causal = causal;
+  a.c2 = softmax_scale * kLog2e;
+  a.num_splits = 1;
+  a.pv = qfa::QK_NVFP4;
+  a.nv_gq = q_tensor_scale;
+  a.nv_gk = k_tensor_scale;
+  return from_hip(qfa::launch_prefill(a, stream));
+}
+
 qfa_status qfa_kv_append(const uint16_t* k_new, const uint16_t* v_new, int B, int Hkv, int n_new, int D,
                          int S_kv_max, int block_size, const int32_t* kv_lens, uint8_t* k4, uint8_t* k4s,
                          uint16_t* kbar, uint8_t* v8, uint8_t* v8s, uint16_t* k_tail, uint16_t* v_tail,
@@ -184,13 +233,12 @@ qfa_status qfa_fwd_decode(const uint8_t* q4, const uint8_t* q4s, const uint8_t* 
                            stream);
 }
 
-qfa_status qfa_fwd_decode_ex(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
-                             const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
-                             int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens, int D,
-                             float softmax_scale, int block_size, int pv_format, int* num_splits, void* workspace,
-                             size_t workspace_bytes, float* O, float* lse, hipStream_t stream) {
+static qfa_status decode_common(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                                const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                                int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens, int D,
+                                float softmax_scale, int block_size, int fmt, float gq, float gk, int* num_splits,
+                                void* workspace, size_t workspace_bytes, float* O, float* lse, hipStream_t stream) {
   if (!num_splits || S_kv_max < 0 || *num_splits < 0 || *num_splits > 4096) return QFA_ERR_INVALID_ARG;
-  if (qfa_status f = check_pv_format(pv_format); f != QFA_OK) return f;
   qfa_status st = check_attn_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, D, softmax_scale,
                                     block_size, O);
   if (st != QFA_OK) return st;
@@ -216,8 +264,32 @@ qfa_status qfa_fwd_decode_ex(const uint8_t* q4, const uint8_t* q4s, const uint8_
   a.causal = 0;
   a.c2 = softmax_scale * kLog2e;
   a.num_splits = splits;
-  a.pv = pv_format;
+  a.pv = fmt;
+  a.nv_gq = gq;
+  a.nv_gk = gk;
   return from_hip(qfa::launch_decode(a, O, lse, stream));
+}
+
+qfa_status qfa_fwd_decode_ex(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                             const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                             int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens, int D,
+                             float softmax_scale, int block_size, int pv_format, int* num_splits, void* workspace,
+                             size_t workspace_bytes, float* O, float* lse, hipStream_t stream) {
+  if (qfa_status f = check_pv_format(pv_format); f != QFA_OK) return f;
+  return decode_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D, softmax_scale,
+                       block_size, pv_format, 1.0f, 1.0f, num_splits, workspace, workspace_bytes, O, lse, stream);
+}
+
+qfa_status qfa_fwd_decode_nvfp4(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                                const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                                int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens, int D,
+                                float softmax_scale, float q_tensor_scale, float k_tensor_scale, int* num_splits,
+                                void* workspace, size_t workspace_bytes, float* O, float* lse, hipStream_t stream) {
+  if (!pow2_ok(q_tensor_scale) || !pow2_ok(k_tensor_scale)) return QFA_ERR_INVALID_ARG;
+  if (!q4 || !q4s) return QFA_ERR_INVALID_ARG;
+  return decode_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D, softmax_scale,
+                       32, qfa::QK_NVFP4, q_tensor_scale, k_tensor_scale, num_splits, workspace, workspace_bytes, O,
+                       lse, stream);
 }
 
 }  // extern "C"

@@ -40,8 +40,8 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
 
   RowState<D> st;
   const size_t qrow = (size_t)b * a.Hq + (rvalid ? h : 0);
-  load_q<D, PV>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * (D / 32) : nullptr,
-            a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid);
+  load_q<D, PV>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * TileLayout<D, PV>::KSB : nullptr,
+                a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid, a.nv_gq, a.nv_gk);
 
   uint8_t* bufs = smem;
   float* dl = reinterpret_cast<float*>(smem + 2 * TL::STRIDE);
@@ -142,6 +142,7 @@ static hipError_t decode_d(const AttnArgs& a, float* O, float* lse, hipStream_t 
     case PV_FP8: return decode_dp<D, PV_FP8>(a, O, lse, s);
     case PV_FP8_BLOCKP: return decode_dp<D, PV_FP8_BLOCKP>(a, O, lse, s);
     case PV_FP4: return decode_dp<D, PV_FP4>(a, O, lse, s);
+    case QK_NVFP4: return decode_dp<D, QK_NVFP4>(a, O, lse, s);
     default: return hipErrorInvalidValue;
   }
 }

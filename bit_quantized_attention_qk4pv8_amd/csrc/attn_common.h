@@ -38,7 +38,16 @@ namespace qfa {
 // and both products run on the FP4 MFMA.  ([FA4tut] "Direct-P": one E8M0
 // scale per 32 probabilities; [MpFA] abstract: FP8 P/V versus fully FP4
 // attention.)
-constexpr int PV_FP8 = 0, PV_FP8_BLOCKP = 1, PV_FP4 = 2;
+// QK_NVFP4: Q and K in NVFP4 (blocks of 16, E4M3 scales, power-of-two tensor
+// scales) with the method's E4M3 P and V.  The K tile keeps the MXFP4 code
+// layout (with twice the scale bytes); each lane decodes its codes to bf16
+// right before the product, exactly (an E2M1 value times an E4M3 scale times
+// a power of two has at most six significant bits), and S runs on the bf16
+// MFMA: an emulation of NVFP4 numerics, not a fast path.  ([MpFA] abstract:
+// NVFP4 for QK; [FA4tut] "FP4 只有约 15 个可表示的数": blocks of 16 with an
+// E4M3 scale and an FP32 tensor scale.)
+// The P/V format of a kernel format: QK_NVFP4 keeps the method's.
+constexpr int pv_of(int fmt) { return fmt == QK_NVFP4 ? PV_FP8 : fmt; }
 // V bytes per (32-token block, channel) record
 template <int PV>
 constexpr int v_record() { return PV == PV_FP4 ? 16 : 32; }
@@ -46,7 +55,8 @@ constexpr int v_record() { return PV == PV_FP4 ? 16 : 32; }
 template <int D, int PV = PV_FP8>
 struct TileLayout {
   static constexpr int KC = kTile * D / 2;
-  static constexpr int KS_BYTES = kTile * D / 32;
+  static constexpr int KSB = PV == QK_NVFP4 ? D / 16 : D / 32;  // K scale bytes per token
+  static constexpr int KS_BYTES = kTile * KSB;
   static constexpr int VC = (kTile / 32) * D * v_record<PV>();
   static constexpr int VS_BYTES = (kTile / 32) * D;
   static constexpr int K_OFF = 0;
@@ -58,7 +68,7 @@ struct TileLayout {
   static constexpr int VREG = VC + 1024;  // V region bytes (codes, then scales at VC)
   static constexpr int NK = KC / 1024;  // 1 KB DMA instructions per region
   static constexpr int NV = VC / 1024;
-  static constexpr int NKS = D == 128 ? 2 : 1;  // dword DMA instructions (256 B each) for K scales
+  static constexpr int NKS = KS_BYTES / 256;  // dword DMA instructions (256 B each) for K scales
   static constexpr int NINS = NK + NKS + NV + 1;
 };
 
@@ -116,11 +126,11 @@ struct TileLoader {
     const int nvb_storage = (L_storage + 31) / 32, nvb = (L_valid + 31) / 32;
     L = L_valid;
     kc = k4 + bg * L_storage * (D / 2);
-    ks = k4s + bg * L_storage * (D / 32);
+    ks = k4s + bg * L_storage * TL::KSB;
     vc = v8 + bg * nvb_storage * D * VR;
     vs = v8s + bg * nvb_storage * D;
     kc_bytes = (uint32_t)L_valid * (D / 2);
-    ks_bytes = (uint32_t)L_valid * (D / 32);
+    ks_bytes = (uint32_t)L_valid * TL::KSB;
     vc_bytes = (uint32_t)nvb * D * VR;
     vs_bytes = (uint32_t)nvb * D;
   }
@@ -245,11 +255,12 @@ struct TileLoader {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, lane * 4, 0, 0, 0);
   }
 
-  // D = 64 with an odd key count: the last token's two scale bytes share a
-  // dword with bytes past the end, which the range check zeroes; patch them
-  // after the DMA has landed (called between the wait and the barrier).
+  // Two scale bytes per token (MXFP4, D = 64) with an odd key count: the last
+  // token's scale bytes share a dword with bytes past the end, which the
+  // range check zeroes; patch them after the DMA has landed (called between
+  // the wait and the barrier).
   __device__ __forceinline__ void fixup(int t, uint8_t* kreg) const {
-    if (D == 64 && (L & 1) && t == (L - 1) / kTile && (threadIdx.x & 63) == 0) {
+    if (TL::KSB == 2 && (L & 1) && t == (L - 1) / kTile && (threadIdx.x & 63) == 0) {
       const int j = (L - 1) - t * kTile;
       kreg[TL::KC + 2 * j] = ks[2 * (L - 1)];
       kreg[TL::KC + 2 * j + 1] = ks[2 * (L - 1) + 1];
@@ -295,7 +306,7 @@ struct LaneOffs {
 #pragma unroll
       for (int k = 0; k < D / 64; ++k) k1[k] = tok * (D / 2) + 16 * (kblock<D>(g, k) ^ sw1);
     }
-    ks = TL::KC + tok * (D / 32) + (D == 128 ? 2 * g : g);
+    ks = TL::KC + tok * TL::KSB + (D == 128 ? 2 * g : g) * (TL::KSB / (D / 32));
     if (PV == PV_FP4)
       v = (g * D + rho) * 16;
     else
@@ -315,11 +326,13 @@ struct RowState {
   float m_ref;     // frame of o and lv: both hold sum 2^(m_t - m_ref) P_t (V_t | 1)
   v8i ones;        // 1.0 in every element (E4M3 0x38, or E2M1 0x2 in the first four dwords): the A
                    // operand of the denominator product
+  bf16x8 qn[D / 16];  // QK_NVFP4: Q decoded to bf16, 8 channels per bf16 MFMA (see qk_blk)
+  float gk;           // QK_NVFP4: K's tensor scale
 };
 
 // The P and V operand types of the P V product: 32 E4M3 bytes or 32 E2M1 nibbles per lane.
 template <int PV>
-using POp = typename std::conditional<PV == PV_FP4, v4i, v8i>::type;
+using POp = typename std::conditional<pv_of(PV) == PV_FP4, v4i, v8i>::type;
 
 // Softmax step of one tile.  s holds S' = Q'K^T, the logits in log2 units
 // (Q carries the factor softmax_scale * log2 e).  Masks keys > jlim (when
@@ -333,6 +346,7 @@ using POp = typename std::conditional<PV == PV_FP4, v4i, v8i>::type;
 template <int D, bool COMP, int PV>
 __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int t, bool need_mask, int jlim,
                                              float d32, POp<PV> (&pb)[2], int (&pscale)[2]) {
+  constexpr int P = pv_of(PV);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   // ---- mask (diagonal / ragged tiles only); score s[c][rr] is key
@@ -362,7 +376,7 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
   // v_max3_f32, one instruction per two scores) and one lane swap
   float mx;
   float bmax[4];  // PV_FP8_BLOCKP: max of key block c (both lanes of the row); PV_FP4: [h] of block 2h + g
-  if constexpr (PV == PV_FP4) {
+  if constexpr (P == PV_FP4) {
     // a lane holds all 32 keys of block 2h + g: its max needs no other lane
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -377,7 +391,7 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
     mx = __builtin_fmaxf(bmax[0], bmax[1]);
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
     mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-  } else if constexpr (PV == PV_FP8) {
+  } else if constexpr (P == PV_FP8) {
     float mx0 = s[0][0], mx1 = s[2][0];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -442,14 +456,14 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
   // that can give a non-zero code (y > e - 18) have 2^y in [2^-118, 2^100].
   // A wave with an exponent outside subtracts it from the scores first.
   float e[4];
-  if constexpr (PV == PV_FP4) {  // e[c]: the exponent of MFMA c's keys (block 2h + g for c = 2h + w)
+  if constexpr (P == PV_FP4) {  // e[c]: the exponent of MFMA c's keys (block 2h + g for c = 2h + w)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float eh = (mn == -__builtin_inff()) ? 0.0f : __builtin_fmaxf(__builtin_ceilf(bmax[h]), mn - 64.0f);
       e[2 * h] = e[2 * h + 1] = eh;
       pscale[h] = (mn == -__builtin_inff()) ? kScaleOne : kScaleOne + (int)(eh - st.m_ref);
     }
-  } else if constexpr (PV == PV_FP8) {
+  } else if constexpr (P == PV_FP8) {
     pscale[0] = pscale[1] = (mn == -__builtin_inff()) ? kScaleOne : kScaleOne + (int)(mn - st.m_ref);
     e[0] = e[1] = e[2] = e[3] = (mn == -__builtin_inff()) ? 0.0f : mn;
   } else {
@@ -467,7 +481,7 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
   }
   bool out_of_range = false;
 #pragma unroll
-  for (int c = 0; c < (PV == PV_FP8 ? 1 : 4); ++c) out_of_range |= __builtin_fabsf(e[c]) > 100.0f;
+  for (int c = 0; c < (P == PV_FP8 ? 1 : 4); ++c) out_of_range |= __builtin_fabsf(e[c]) > 100.0f;
   const bool far = __builtin_amdgcn_ballot_w64(out_of_range) != 0;
   if (far) {
 #pragma unroll
@@ -477,11 +491,11 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
   }
   // the conversion's scale: 2^(e - 8) for E4M3 (codes 256 * 2^(y - e)),
   // 2^(e - 2) for E2M1 (codes 4 * 2^(y - e))
-  constexpr int PB = PV == PV_FP4 ? 2 : 8;
+  constexpr int PB = P == PV_FP4 ? 2 : 8;
   float cs[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) cs[c] = far ? (PV == PV_FP4 ? 0x1p-2f : 0x1p-8f) : __builtin_ldexpf(1.0f, (int)e[c] - PB);
-  if constexpr (PV == PV_FP4) {
+  for (int c = 0; c < 4; ++c) cs[c] = far ? (P == PV_FP4 ? 0x1p-2f : 0x1p-8f) : __builtin_ldexpf(1.0f, (int)e[c] - PB);
+  if constexpr (P == PV_FP4) {
     // pb[h] register r holds keys 8r .. 8r+7 of block 2h + g (s[2h + r/2][8(r%2) ..]),
     // two E2M1 codes per byte, the lower key in the low nibble
 #pragma unroll
@@ -537,19 +551,50 @@ __device__ __forceinline__ void load_k_blk(const uint8_t* kreg, const LaneOffs<D
     const uint32_t lk = (PV == PV_FP4 && (c & 1)) ? lo.k1[PV == PV_FP4 ? kk : 0] : lo.k[kk];
     k.ka[kk] = *reinterpret_cast<const v4i*>(kreg + lk + t0 * (D / 2));
   }
-  if (D == 128)
-    k.sc = *reinterpret_cast<const uint16_t*>(kreg + lo.ks + t0 * (D / 32));
-  else
-    k.sc = kreg[lo.ks + t0 * (D / 32)];
+  using TL = TileLayout<D, PV>;
+  const uint8_t* sp = kreg + lo.ks + t0 * TL::KSB;
+  if (PV == QK_NVFP4)  // four (D = 128) or two E4M3 scales of this lane's channels
+    k.sc = D == 128 ? (int)*reinterpret_cast<const uint32_t*>(sp) : (int)*reinterpret_cast<const uint16_t*>(sp);
+  else                 // two (D = 128) or one E8M0 scale
+    k.sc = D == 128 ? (int)*reinterpret_cast<const uint16_t*>(sp) : (int)*sp;
 }
 
 // S^T block c = K_c Q^T: sc_[rr] is the score of this lane's row (l % 32)
 // against key 32c + 16g + rr of the tile (g = l / 32).
-template <int D>
+// QK_NVFP4: eight E2M1 codes (one dword, channels 8r .. 8r+7 of a 32-channel
+// chunk) times their E4M3 block scale s times the tensor scale g, as bf16.
+// The scaled FP4 conversions apply only the exponent of their scale operand
+// (an E8M0 scale), so the codes are converted with g (a power of two) to
+// binary32, multiplied by s there (exact: at most six significant bits) and
+// packed to bf16 (exact for the same reason).
+__device__ __forceinline__ bf16x8 nvfp4_decode8(uint32_t w, float s, float g) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, g, 0);
+  const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, g, 1);
+  const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, g, 2);
+  const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, g, 3);
+  return bf16x8{(__bf16)(p0[0] * s), (__bf16)(p0[1] * s), (__bf16)(p1[0] * s), (__bf16)(p1[1] * s),
+                (__bf16)(p2[0] * s), (__bf16)(p2[1] * s), (__bf16)(p3[0] * s), (__bf16)(p3[1] * s)};
+}
+
+template <int D, int PV = PV_FP8>
 __device__ __forceinline__ void qk_blk(const RowState<D>& st, const KBlk<D>& k, v16f& sc_) {
   sc_ = v16f{};
-  sc_ = mfma_fp4_32x32x64_sel<0>(k.ka[0], st.qa[0], sc_, k.sc, st.qs);
-  if (D == 128) sc_ = mfma_fp4_32x32x64_sel<1>(k.ka[D / 64 - 1], st.qa[D / 64 - 1], sc_, k.sc, st.qs);
+  if constexpr (PV == QK_NVFP4) {
+    // lane group g holds chunk kblock(g, kk) (32 channels); bf16 MFMA 4kk + r
+    // contracts its channels 8r .. 8r+7 against the same channels of Q
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s = e4m3_byte_to_f32(k.sc, 2 * kk + (r >> 1));
+        const bf16x8 a = nvfp4_decode8((uint32_t)k.ka[kk][r], s, st.gk);
+        sc_ = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qn[4 * kk + r], sc_, 0, 0, 0);
+      }
+  } else {
+    sc_ = mfma_fp4_32x32x64_sel<0>(k.ka[0], st.qa[0], sc_, k.sc, st.qs);
+    if (D == 128) sc_ = mfma_fp4_32x32x64_sel<1>(k.ka[D / 64 - 1], st.qa[D / 64 - 1], sc_, k.sc, st.qs);
+  }
 }
 
 // One V operand (64 keys x 32 channels: half h = q / (D/32), channel block
@@ -624,7 +669,7 @@ __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     __builtin_amdgcn_sched_barrier(0);
-    qk_blk<D>(st, kb[c & 1], s[c]);
+    qk_blk<D, PV>(st, kb[c & 1], s[c]);
     if (c + 2 < 4) load_k_blk<D, PV>(kreg, lo, c + 2, kb[c & 1]);
     hook(NQ + c);
   }
@@ -662,7 +707,7 @@ __device__ __forceinline__ void qk_tile(const RowState<D>& st, const LaneOffs<D,
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     __builtin_amdgcn_sched_barrier(0);
-    qk_blk<D>(st, kb[c & 1], s[c]);
+    qk_blk<D, PV>(st, kb[c & 1], s[c]);
     if (c + 2 < 4) load_k_blk<D, PV>(kreg, lo, c + 2, kb[c & 1]);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -731,12 +776,26 @@ __device__ __forceinline__ void compute_delta(float* dl, const uint16_t* kbar_bg
 // Q fragments of this lane's row (zeros when invalid) and a fresh row state.
 // With q4row null, the row is quantised here from its bf16 values qbfrow
 // (times c2, then the MXFP4 block rule): the same bytes the quantiser kernel
-// writes for Q with prescale c2.
+// writes for Q with prescale c2.  QK_NVFP4 takes the quantised row (codes, E4M3
+// scales) and the tensor scales gq, gk, and keeps Q as bf16.
 template <int D, int PV = PV_FP8>
 __device__ __forceinline__ void load_q(RowState<D>& st, const uint8_t* q4row, const uint8_t* q4srow,
-                                       const uint16_t* qbfrow, float c2, bool valid) {
+                                       const uint16_t* qbfrow, float c2, bool valid, float gq = 1.0f,
+                                       float gk = 1.0f) {
   const int g = (threadIdx.x & 63) >> 5;
   st.qs = 0;
+  if constexpr (PV == QK_NVFP4) {  // NVFP4 Q (codes and E4M3 scales) decoded to bf16
+    st.gk = gk;
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) {
+      const int b = kblock<D>(g, kk);
+      const v4i c = valid ? *reinterpret_cast<const v4i*>(q4row + 16 * b) : v4i{0, 0, 0, 0};
+      const int sc = valid ? (int)*reinterpret_cast<const uint16_t*>(q4srow + 2 * b) : 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        st.qn[4 * kk + r] = nvfp4_decode8((uint32_t)c[r], e4m3_byte_to_f32(sc, r >> 1), gq);
+    }
+  } else {
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) {
     const int b = kblock<D>(g, k);
@@ -756,6 +815,7 @@ __device__ __forceinline__ void load_q(RowState<D>& st, const uint8_t* q4row, co
       st.qa[k] = v4i{(int)c.x, (int)c.y, (int)c.z, (int)c.w};
       st.qs |= (int)sc << (8 * k);
     }
+  }
   }
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) st.o[cb] = v16f{};

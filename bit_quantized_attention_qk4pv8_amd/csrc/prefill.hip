@@ -162,8 +162,8 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   // while they are in flight
   for (int j = 0; j < NB - 1 && j < T; ++j) ld.issue_k(j, kbuf + j * TL::KREG, wave);
   for (int j = 0; j < NB - 2 && j < T; ++j) ld.issue_v(j, vbuf + j * TL::VREG, wave);
-  load_q<D, PV>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * (D / 32) : nullptr,
-            a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid);
+  load_q<D, PV>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * TileLayout<D, PV>::KSB : nullptr,
+                a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid, a.nv_gq, a.nv_gk);
   wait_vmem_le(0);
   __syncthreads();  // every wave's loads have landed before the scale patch
   if (wave == 0) {
@@ -258,6 +258,7 @@ static hipError_t prefill_d(const AttnArgs& a, hipStream_t s) {
     case PV_FP8: return prefill_dp<D, PV_FP8>(a, s);
     case PV_FP8_BLOCKP: return prefill_dp<D, PV_FP8_BLOCKP>(a, s);
     case PV_FP4: return prefill_dp<D, PV_FP4>(a, s);
+    case QK_NVFP4: return prefill_dp<D, QK_NVFP4>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -77,6 +77,56 @@ __device__ __forceinline__ void mxfp4_block(const float (&v)[kBlock], uint4& cod
   scale = (uint8_t)(e + 127);
 }
 
+// E4M3 byte `sel` (0..3, a constant after unrolling) of w as binary32 (exact).
+__device__ __forceinline__ float e4m3_byte_to_f32(int w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
+  }
+}
+
+// One NVFP4 block: 16 binary32 values -> 8 bytes of E2M1 codes (element 2k in
+// the low nibble of byte k) and the E4M3 scale code, with the per-tensor scale
+// g (a power of two).  The scale is the E4M3 code (RNE, saturating at 448) of
+// fl32(fl32(amax / g) / 6), each element the E2M1 code (RNE, saturating at 6)
+// of fl32(x / (s g)): both divisions are IEEE binary32 ones (correctly
+// rounded), so the decisions are those of the binary32 definition.  A zero
+// scale gives zero codes; a non-finite block gets scale 0x7F and zero codes.
+// Used by the NVFP4 quantiser; the attention kernels only decode.
+__device__ __forceinline__ void nvfp4_block(const float (&v)[16], float g, uint2& codes, uint8_t& scale) {
+  uint32_t amax = 0u, nonfinite = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t a = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+    nonfinite |= (a >= 0x7F800000u);
+    amax = a > amax ? a : amax;
+  }
+  codes = make_uint2(0u, 0u);
+  scale = 0x7F;
+  if (nonfinite) return;
+  const float q = __builtin_fminf((__uint_as_float(amax) / g) / 6.0f, 448.0f);
+  const int sc = __builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xFF;
+  scale = (uint8_t)sc;
+  const float t = __builtin_amdgcn_cvt_f32_fp8(sc, 0) * g;
+  if (t == 0.0f) return;
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float q8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q8[j] = __builtin_fminf(__builtin_fmaxf(v[8 * h + j] / t, -6.0f), 6.0f);
+    uint32_t r = 0u;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q8[0], q8[1], 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q8[2], q8[3], 1.0f, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q8[4], q8[5], 1.0f, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q8[6], q8[7], 1.0f, 3);
+    w[h] = r;
+  }
+  codes = make_uint2(w[0], w[1]);
+}
+
 // 32 consecutive bf16 values (64 bytes, 16-byte aligned) -> binary32.
 __device__ __forceinline__ void load_bf16_block(const uint16_t* src, float (&v)[kBlock]) {
 #pragma unroll
@@ -116,8 +166,14 @@ hipError_t launch_quant_qk4(const uint16_t* x, int B, int H, int S, int D, int s
                             uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t s);
 hipError_t launch_quant_v8(const uint16_t* v, int B, int H, int S, int D, uint8_t* codes, uint8_t* scales,
                            hipStream_t s);
+hipError_t launch_quant_nvfp4(const uint16_t* x, int B, int H, int S, int D, int smooth, float prescale, float g,
+                              uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t s);
 hipError_t launch_quant_v4(const uint16_t* v, int B, int H, int S, int D, uint8_t* codes, uint8_t* scales,
                            hipStream_t s);
+
+// Kernel formats (the attention kernels' template argument; see attn_common.h):
+// the method, two P/V contrast formats, and NVFP4 Q/K with the method's P/V.
+constexpr int PV_FP8 = 0, PV_FP8_BLOCKP = 1, PV_FP4 = 2, QK_NVFP4 = 3;
 
 struct AttnArgs {
   const uint8_t* q4;
@@ -135,7 +191,8 @@ struct AttnArgs {
   int causal;
   float c2;               // softmax_scale * log2(e), rounded to binary32
   int num_splits;         // decode
-  int pv;                 // P/V format (PV_FP8, PV_FP8_BLOCKP, PV_FP4)
+  int pv;                 // kernel format (PV_FP8, PV_FP8_BLOCKP, PV_FP4, QK_NVFP4)
+  float nv_gq, nv_gk;     // QK_NVFP4: the tensor scales of Q and K (powers of two)
 };
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);

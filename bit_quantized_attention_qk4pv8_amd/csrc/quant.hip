@@ -81,6 +81,60 @@ __global__ void __launch_bounds__(256) k_quant_qk4(const uint16_t* __restrict__ 
   }
 }
 
+// Q/K -> NVFP4 (the QK format of the NVFP4 contrast case): as k_quant_qk4 with
+// blocks of 16 channels, E4M3 block scales and the per-tensor scale g.
+template <int D>
+__global__ void __launch_bounds__(256) k_quant_nvfp4(const uint16_t* __restrict__ x, int S, int ntiles, int smooth,
+                                                     float prescale, float g, uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales, uint16_t* __restrict__ kbar) {
+  constexpr int NB = D / 16;
+  __shared__ float kb[D];
+  const int tile = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int t0 = tile * kTile;
+  const int n = min(kTile, S - t0);
+  const uint16_t* xs = x + (bh * (size_t)S + t0) * D;
+  if (smooth) {
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+      double sum = 0.0;
+      for (int j = 0; j < n; ++j) sum += (double)bf16_bits_to_float(xs[(size_t)j * D + c]);
+      uint16_t b = f64_to_bf16_rne(sum / (double)n);
+      kb[c] = bf16_bits_to_float(b);
+      kbar[(bh * ntiles + tile) * D + c] = b;
+    }
+    __syncthreads();
+  }
+  for (int w = threadIdx.x; w < n * NB; w += blockDim.x) {
+    const int j = w / NB, blk = w % NB;
+    float v[16];
+    const uint16_t* src = xs + (size_t)j * D + blk * 16;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint4 u = reinterpret_cast<const uint4*>(src)[q];
+      const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[q * 8 + 2 * k] = bf16_bits_to_float(wds[k] & 0xFFFFu);
+        v[q * 8 + 2 * k + 1] = bf16_bits_to_float(wds[k] >> 16);
+      }
+    }
+    if (smooth) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = v[i] - kb[blk * 16 + i];
+    }
+    if (prescale != 1.0f) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = v[i] * prescale;
+    }
+    const size_t row = bh * (size_t)S + t0 + j;
+    uint2 out;
+    uint8_t sc;
+    nvfp4_block(v, g, out, sc);
+    *reinterpret_cast<uint2*>(codes + row * (D / 2) + blk * 8) = out;
+    scales[row * NB + blk] = sc;
+  }
+}
+
 // One V record: the 32 token values of one channel (missing tokens 0) -> 32
 // E4M3 codes, RNE by the hardware converter on the exact x * 2^-e, and the
 // E8M0 code of e = ceil(log2 amax) - 8; a non-finite record gets scale 0xFF
@@ -314,6 +368,24 @@ hipError_t launch_quant_v8(const uint16_t* v, int B, int H, int S, int D, uint8_
     QFA_V8_CASE(32) QFA_V8_CASE(64) QFA_V8_CASE(96) QFA_V8_CASE(128) QFA_V8_CASE(160) QFA_V8_CASE(192)
     QFA_V8_CASE(224) QFA_V8_CASE(256)
 #undef QFA_V8_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4(const uint16_t* x, int B, int H, int S, int D, int smooth, float prescale, float g,
+                              uint8_t* codes, uint8_t* scales, uint16_t* kbar, hipStream_t s) {
+  const int ntiles = (S + kTile - 1) / kTile;
+  dim3 grid(ntiles, B * H);
+  switch (D) {
+#define QFA_NV_CASE(DD)                                                                                       \
+  case DD:                                                                                                    \
+    hipLaunchKernelGGL(k_quant_nvfp4<DD>, grid, dim3(256), 0, s, x, S, ntiles, smooth, prescale, g, codes, scales, \
+                       kbar);                                                                                 \
+    break;
+    QFA_NV_CASE(32) QFA_NV_CASE(64) QFA_NV_CASE(96) QFA_NV_CASE(128) QFA_NV_CASE(160) QFA_NV_CASE(192)
+    QFA_NV_CASE(224) QFA_NV_CASE(256)
+#undef QFA_NV_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

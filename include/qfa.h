@@ -231,6 +231,41 @@ qfa_status qfa_kv_append(const uint16_t* k_new, const uint16_t* v_new, int B, in
                          uint16_t* kbar, uint8_t* v8, uint8_t* v8s, uint16_t* k_tail, uint16_t* v_tail,
                          hipStream_t stream);
 
+/*
+ * NVFP4 contrast case for Q and K (MpFA abstract: NVFP4 for QK; the FP4
+ * tutorial's section "FP4 只有约 15 个可表示的数": blocks of 16 values with an
+ * E4M3 scale and a per-tensor FP32 scale, about 4.5 bits per value).
+ *
+ * qfa_quantize_nvfp4: x -> E2M1 codes [B][H][S][D/2] (element 2k in the low
+ * nibble of byte k) and E4M3 block scales [B][H][S][D/16].  block_size must
+ * be 16.  tensor_scale g must be a positive power of two (else
+ * QFA_ERR_INVALID_ARG); the smallest 2^k with amax / (6 * 2^k) <= 448 uses
+ * E4M3's whole range.  Per block of 16 values (after smoothing and prescale,
+ * as for qfa_quantize_qk4) the scale is the E4M3 code (RNE, saturating at 448)
+ * of fl32(fl32(amax / g) / 6) and each value the E2M1 code (RNE, saturating at
+ * 6) of fl32(x / (s g)).  A scale of 0 gives zero codes; a block holding a
+ * non-finite value gets scale 0x7F (E4M3 NaN) and zero codes.
+ *
+ * qfa_fwd_prefill_nvfp4 / qfa_fwd_decode_nvfp4: qfa_fwd_prefill / qfa_fwd_decode
+ * with Q and K in NVFP4 (q4 and q4s required, from qfa_quantize_nvfp4 with
+ * prescale qfa_exp2_scale(softmax_scale) and tensor scale q_tensor_scale; K
+ * with k_tensor_scale) and P and V as in the method.  S is computed exactly
+ * from the decoded values (each lane decodes to bf16 and S runs on the bf16
+ * MFMA): an emulation of NVFP4 numerics on gfx950, slower than the MXFP4 path.
+ */
+qfa_status qfa_quantize_nvfp4(const uint16_t* x, int B, int H, int S, int D, int block_size, int smooth,
+                              float prescale, float tensor_scale, uint8_t* codes, uint8_t* scales, uint16_t* kbar,
+                              hipStream_t stream);
+qfa_status qfa_fwd_prefill_nvfp4(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                                 const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                                 int B, int Hq, int Hkv, int S_q, int S_kv, int D, int causal, float softmax_scale,
+                                 float q_tensor_scale, float k_tensor_scale, float* O, float* lse, hipStream_t stream);
+qfa_status qfa_fwd_decode_nvfp4(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                                const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8, const uint8_t* v8s,
+                                int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens, int D,
+                                float softmax_scale, float q_tensor_scale, float k_tensor_scale, int* num_splits,
+                                void* workspace, size_t workspace_bytes, float* O, float* lse, hipStream_t stream);
+
 /* Bytes of decode workspace for the given shape and split count (> 0). */
 size_t qfa_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 

@@ -146,6 +146,36 @@ def test_pv_format_validation():
                      F(0.125), 32, fake, None, None) == qfa.QFA_ERR_INVALID_ARG
 
 
+def test_nvfp4_validation_and_tensor_scale():
+    P = ctypes.c_void_p
+    F = ctypes.c_float
+    fake = P(4096)
+    q = lambda bs=16, g=1.0, smooth=0, kbar=None: _call_raw(
+        "qfa_quantize_nvfp4", fake, 1, 1, 1, 64, bs, smooth, F(1.0), F(g), fake, fake, kbar, None)
+    assert q(bs=32) == qfa.QFA_ERR_UNSUPPORTED
+    for bad in (0.0, -2.0, 3.0, 0.75, float("inf"), float("nan")):
+        assert q(g=bad) == qfa.QFA_ERR_INVALID_ARG                    # the tensor scale is a power of two
+    assert q(smooth=1) == qfa.QFA_ERR_INVALID_ARG                       # smoothing needs kbar
+    assert _call_raw("qfa_quantize_nvfp4", None, 0, 1, 1, 64, 16, 0, F(1.0), F(0.5), None, None, None,
+                     None) == qfa.QFA_OK
+    pre = lambda q4, q4s, gq=1.0: _call_raw(
+        "qfa_fwd_prefill_nvfp4", q4, q4s, fake, fake, None, fake, fake, fake, 1, 4, 2, 8, 8, 128, 1, F(0.125),
+        F(gq), F(1.0), fake, None, None)
+    assert pre(None, None) == qfa.QFA_ERR_INVALID_ARG                   # NVFP4 Q comes quantised
+    assert pre(fake, fake, gq=3.0) == qfa.QFA_ERR_INVALID_ARG
+    ns = ctypes.c_int(4)
+    assert _call_raw("qfa_fwd_decode_nvfp4", fake, fake, fake, fake, None, None, fake, fake, 2, 8, 2, 1024, None,
+                     128, F(0.1), F(1.0), F(0.25), ctypes.byref(ns), fake, ctypes.c_size_t(16), fake, None,
+                     None) == qfa.QFA_ERR_WORKSPACE
+    # the host helper picks the smallest power of two g with amax / (6 g) <= 448
+    assert qfa.nvfp4_tensor_scale(6 * 448.0) == 1.0
+    assert qfa.nvfp4_tensor_scale(6 * 448.0 * 1.0001) == 2.0
+    assert qfa.nvfp4_tensor_scale(0.0) == 1.0
+    for amax in (1e-3, 0.37, 5.0, 1234.5, 1e6):
+        g = qfa.nvfp4_tensor_scale(amax)
+        assert amax / (6 * g) <= 448.0 < amax / (6 * g / 2)
+
+
 def test_kv_append_validation():
     P = ctypes.c_void_p
     fake, odd = P(4096), P(4097)

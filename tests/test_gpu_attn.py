@@ -350,3 +350,92 @@ def test_decode_pv_formats(smooth, pv):
 def test_decode_fp4_d64():
     q, k, v = _rand_inputs(2, 4, 4, 1, 300, 64, seed=24)
     _check_decode(q, k, v, 7, label="decode-fp4-d64", pv=qfa.QFA_PV_FP4)
+
+
+# ----------------------------------------------------------------------------- NVFP4 Q/K
+def _nv_scales(q, k, scale):
+    c2 = qfa.qfa_exp2_scale(scale)
+    gq = qfa.nvfp4_tensor_scale(float((q.float() * c2).abs().max()))
+    gk = qfa.nvfp4_tensor_scale(float(k.float().abs().max()))
+    return c2, gq, gk
+
+
+def _check_prefill_nv(q, k, v, causal, scale, smooth, rows, label):
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    say("prefill-nvfp4", label, "q", tuple(q.shape), "k", tuple(k.shape), "causal", causal, "smooth", smooth)
+    c2, gq, gk = _nv_scales(q, k, scale)
+    if smooth:  # the tensor scale of the smoothed K
+        kb = bf16_bits(k)
+        _, _, kbar_o = oracle.quantize_qk4(kb, smooth=True)
+        ks = oracle.bf16_to_f64(kb) - np.repeat(oracle.bf16_to_f64(kbar_o), 128, axis=2)[:, :, :Skv]
+        gk = qfa.nvfp4_tensor_scale(float(np.abs(ks).max()))
+    q4, q4s, _ = qfa.quantize_nvfp4(q, gq, prescale=c2)
+    k4, k4s, kbar = qfa.quantize_nvfp4(k, gk, smooth=smooth)
+    v8, v8s = qfa.quantize_v8(v)
+    O = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    qfa.qfa_fwd_prefill_nvfp4(q4, q4s, k4, k4s, kbar, q if smooth else None, v8, v8s, B, Hq, Hkv, Sq, Skv, D,
+                              causal, scale, gq, gk, O, lse)
+    torch.cuda.synchronize()
+    res = oracle.prefill_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, causal, scale, smooth=smooth,
+                              nvfp4=(gq, gk))
+    Og = to_np(O)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    lg = to_np(lse)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    compare_o(Og, res["O_q"], lg, res["lse_q"], label)
+    ok = np.isfinite(res["lse_x"])
+    if ok.any():
+        ex = res["O_x"][ok]
+        say("%s vs exact FP64: rel-L2 %.3e (reported only)" % (label, np.linalg.norm(Og[ok] - ex) / np.linalg.norm(ex)))
+
+
+NV_CASES = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, smooth, label
+    (1, 4, 1, 333, 333, 128, True, False, "nv-causal-ragged-G4"),
+    (2, 5, 1, 70, 700, 64, False, False, "nv-d64-G5"),
+    (1, 4, 2, 300, 200, 128, True, False, "nv-sq>skv"),
+    (1, 2, 1, 200, 600, 128, True, True, "nv-compensation"),
+]
+
+
+@pytest.mark.parametrize("case", NV_CASES, ids=[c[-1] for c in NV_CASES])
+def test_prefill_nvfp4_small_all_rows(case):
+    B, Hq, Hkv, Sq, Skv, D, causal, smooth, label = case
+    q, k, v = _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed=zlib.crc32(label.encode()) % 1000,
+                           k_offset=3.0 if smooth else 0.0, q_scale=2.0)
+    _check_prefill_nv(q, k, v, causal, 1.0 / math.sqrt(D), smooth, _all_rows(B, Hq, Sq), label)
+
+
+def test_decode_nvfp4_varlen():
+    B, Hq, Hkv, Smax, D = 3, 8, 2, 1000, 128
+    q, k, v = _rand_inputs(B, Hq, Hkv, 1, Smax, D, seed=25, q_scale=2.0)
+    kv_lens = [1000, 517, 0]
+    scale = 1.0 / math.sqrt(D)
+    c2, gq, gk = _nv_scales(q, k, scale)
+    say("decode-nvfp4 varlen", tuple(k.shape), kv_lens)
+    q4, q4s, _ = qfa.quantize_nvfp4(q, gq, prescale=c2)
+    k4 = torch.zeros((B, Hkv, Smax, D // 2), dtype=torch.uint8, device="cuda")
+    k4s = torch.zeros((B, Hkv, Smax, D // 16), dtype=torch.uint8, device="cuda")
+    v8 = torch.zeros((B, Hkv, (Smax + 31) // 32, D, 32), dtype=torch.uint8, device="cuda")
+    v8s = torch.zeros((B, Hkv, (Smax + 31) // 32, D), dtype=torch.uint8, device="cuda")
+    for b, L in enumerate(kv_lens):   # each sequence's own tokens, as the cache writer stores them
+        if L:
+            kc, ksc, _ = qfa.quantize_nvfp4(k[b:b + 1, :, :L].contiguous(), gk)
+            vc, vsc = qfa.quantize_v8(v[b:b + 1, :, :L].contiguous())
+            k4[b:b + 1, :, :L], k4s[b:b + 1, :, :L] = kc, ksc
+            v8[b:b + 1, :, :vc.shape[2]], v8s[b:b + 1, :, :vsc.shape[2]] = vc, vsc
+    lens = torch.tensor(kv_lens, dtype=torch.int32, device="cuda")
+    splits = 3
+    wsb = qfa.qfa_decode_workspace_bytes(B, Hq, D, splits)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    O = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    used = qfa.qfa_fwd_decode_nvfp4(q4, q4s, k4, k4s, None, None, v8, v8s, B, Hq, Hkv, Smax, lens, D, scale, gq, gk,
+                                    splits, ws, wsb, O, lse)
+    torch.cuda.synchronize()
+    assert used == splits
+    rows = np.array([(b, h, 0) for b in range(B) for h in range(Hq)], dtype=np.int64)
+    res = oracle.decode_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, scale, used, kv_lens=kv_lens,
+                             nvfp4=(gq, gk))
+    compare_o(to_np(O)[rows[:, 0], rows[:, 1]], res["O_q"], to_np(lse)[rows[:, 0], rows[:, 1]], res["lse_q"],
+              "decode-nvfp4")

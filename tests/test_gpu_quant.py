@@ -72,6 +72,33 @@ def test_v4_bitexact_shapes(shape):
     _check_v4(v.to(torch.bfloat16), "shape%s" % (shape,))
 
 
+def _check_nvfp4(x: torch.Tensor, smooth: bool, label: str, prescale: float = 1.0):
+    xs = x.float() * prescale if prescale != 1.0 else x.float()
+    g = qfa.nvfp4_tensor_scale(float(xs.abs().nan_to_num(0.0, 0.0, 0.0).max()))
+    say("quantize_nvfp4", label, tuple(x.shape), "smooth", smooth, "prescale", prescale, "g", g)
+    codes, scales, kbar = qfa.quantize_nvfp4(x, g, smooth=smooth, prescale=prescale)
+    torch.cuda.synchronize()
+    oc, os_, ok = oracle.quantize_nvfp4(bf16_bits(x), g, smooth=smooth, prescale=prescale)
+    assert np.array_equal(to_np(codes), oc), label + ": codes differ"
+    assert np.array_equal(to_np(scales), os_), label + ": scales differ"
+    if smooth:
+        assert np.array_equal(to_np(kbar.view(torch.int16)).view(np.uint16), ok), label + ": kbar differs"
+
+
+@pytest.mark.parametrize("shape,smooth", [((1, 2, 300, 64), False), ((1, 3, 1000, 128), False),
+                                          ((2, 2, 300, 128), True), ((1, 1, 77, 256), False)])
+def test_nvfp4_bitexact_shapes(shape, smooth):
+    g = torch.Generator(device="cuda").manual_seed(sum(shape) + 3)
+    x = torch.randn(shape, generator=g, device="cuda")
+    x[..., 3] *= 40.0
+    x[..., 0, :] = 0.0
+    x[..., 5, 16:32] *= 1e-4
+    x += torch.randn((1, shape[1], 1, shape[3]), generator=g, device="cuda") * 3.0 * smooth
+    xb = x.to(torch.bfloat16)
+    _check_nvfp4(xb, smooth, "shape%s" % (shape,))
+    _check_nvfp4(xb, False, "shape%s.prescaled" % (shape,), prescale=oracle.exp2_scale(0.0883883))
+
+
 def test_quantizers_nonfinite_and_tiny():
     x = torch.randn((1, 1, 64, 128), device="cuda")
     x[0, 0, 1, 5] = float("nan")
@@ -83,6 +110,7 @@ def test_quantizers_nonfinite_and_tiny():
     _check_qk4(xb, False, "nonfinite.prescaled", prescale=oracle.exp2_scale(0.125))
     _check_v8(xb, "nonfinite")
     _check_v4(xb, "nonfinite")
+    _check_nvfp4(xb, False, "nonfinite")
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama16k", "qwen32k"])
