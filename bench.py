@@ -18,10 +18,11 @@ with HIP events on the stream it is launched on; its peak is the blended
 MXFP4 (Q K^T) / FP8 (P V) MFMA peak.  The CPU baseline is the oracle timed on
 a bounded sample of rows of the same workload on this host (about 15 s).
 
-The two P/V contrast formats (FP8 P with a scale per (row, 32 keys); MXFP4 P
-and V) are timed on the same workloads, kernels only, and reported under
-"variants" with their own roofline fractions (the MXFP4 prefill against the
-all-MXFP4 MFMA peak, the MXFP4 decode against the smaller cache).
+The contrast formats (FP8 P with a scale per (row, 32 keys); MXFP4 P and V;
+NVFP4 Q and K) are timed on the same workloads, kernels only, and reported
+under "variants" with their own roofline fractions (the MXFP4 prefill against
+the all-MXFP4 MFMA peak, the NVFP4 one with Q K^T at the bf16 peak it is
+emulated on, each decode against its own cache bytes).
 
 `--only prefill|decode` runs just that half (for hardware-counter passes);
 `--only copy` runs a plain device-to-device copy of 1 GiB, the reference
@@ -211,6 +212,33 @@ def main():
                                 "unit": "TFLOP/s", "frac": round(vach / vpeak, 4),
                                 "kernel": "qfa::k_prefill<128,%s,%d>" % ("true" if w.smooth else "false", pv)}}
                 del vq, vqs
+            # NVFP4 Q and K (emulated on the bf16 MFMA), P and V as in the method
+            c2 = qfa.qfa_exp2_scale(w.scale)
+            gq = qfa.nvfp4_tensor_scale(float((q.float() * c2).abs().max()))
+            gk = qfa.nvfp4_tensor_scale(float(k.float().abs().max()))
+            q4n, q4ns, _ = qfa.quantize_nvfp4(q, gq, prescale=c2)
+            k4n, k4ns, kbn = qfa.quantize_nvfp4(k, gk, smooth=w.smooth)
+            qfa.qfa_quantize_v8(v, B, Hkv, S, D, 32, v8, v8s, stream)
+            vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for i in range(args.warmup + args.steps):
+                j = i - args.warmup
+                if j >= 0:
+                    vev[j][0].record(stream)
+                qfa.qfa_fwd_prefill_nvfp4(q4n, q4ns, k4n, k4ns, kbn, q if w.smooth else None, v8, v8s, B, Hq, Hkv,
+                                          S, S, D, int(w.causal), w.scale, gq, gk, O, lse, stream)
+                if j >= 0:
+                    vev[j][1].record(stream)
+            torch.cuda.synchronize()
+            vk = float(np.mean([a.elapsed_time(b) for a, b in vev]))
+            vach = (flops + comp) / (vk * 1e-3) / 1e12
+            vpeak = rl.blended_peak(flops, comp, qk_bf16=True) / 1e12
+            out["variants"]["nvfp4_qk"] = {
+                "prefill": {"kernel_ms": round(vk, 4), "achieved": round(vach, 2), "peak": round(vpeak, 2),
+                            "unit": "TFLOP/s", "frac": round(vach / vpeak, 4),
+                            "kernel": "qfa::k_prefill<128,%s,3>" % ("true" if w.smooth else "false"),
+                            "note": "Q K^T emulated on the bf16 MFMA; peak counts it at bf16"}}
+            del q4n, q4ns, k4n, k4ns, kbn
         del O, lse
     # ------------------------------------------------------------------ decode half
     if args.only in ("all", "decode") and not args.no_decode:
@@ -284,7 +312,34 @@ def main():
                 out.setdefault("variants", {}).setdefault(name, {})["decode"] = {
                     "kernel_ms": round(vk, 4), "achieved": round(vg, 1), "peak": rl.PEAK_HBM / 1e9, "unit": "GB/s",
                     "frac": round(vg * 1e9 / rl.PEAK_HBM, 4), "algorithmic_bytes_per_launch": vb}
-            del vd
+            # NVFP4 K cache and Q (P and V as in the method)
+            dq = make_inputs(wd, seed=0, device=dev)
+            c2 = qfa.qfa_exp2_scale(wd.scale)
+            gq = qfa.nvfp4_tensor_scale(float((dq["q"].float() * c2).abs().max()))
+            gk = qfa.nvfp4_tensor_scale(float(dq["k"].float().abs().max()))
+            q4n, q4ns, _ = qfa.quantize_nvfp4(dq["q"], gq, prescale=c2)
+            k4n, k4ns, _ = qfa.quantize_nvfp4(dq["k"], gk)
+            del v8d, v8sd
+            v8d, v8sd = qfa.quantize_v8(vd)
+            del dq
+            vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for i in range(args.warmup + args.steps):
+                j = i - args.warmup
+                if j >= 0:
+                    vev[j][0].record(stream)
+                qfa.qfa_fwd_decode_nvfp4(q4n, q4ns, k4n, k4ns, None, None, v8d, v8sd, Bd, Hqd, Hkvd, L, None, Dd,
+                                         wd.scale, gq, gk, splits, ws, wsb, Od, lsed, stream)
+                if j >= 0:
+                    vev[j][1].record(stream)
+            torch.cuda.synchronize()
+            vk = float(np.mean([a.elapsed_time(b) for a, b in vev]))
+            vb = rl.decode_algorithmic_bytes(Bd, Hqd, Hkvd, L, Dd, k_nvfp4=True)
+            vg = vb / (vk * 1e-3) / 1e9
+            out["variants"].setdefault("nvfp4_qk", {})["decode"] = {
+                "kernel_ms": round(vk, 4), "achieved": round(vg, 1), "peak": rl.PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": round(vg * 1e9 / rl.PEAK_HBM, 4), "algorithmic_bytes_per_launch": vb}
+            del q4n, q4ns, k4n, k4ns, vd
         del k4d, v8d, ws
     # ------------------------------------------------------------------ CPU baseline (oracle)
     if args.only in ("all", "prefill") and not args.no_cpu_baseline:

@@ -28,20 +28,24 @@ def kv_cache_bytes(layers: int, kv_heads: int, head_dim: int, seq_len: int, byte
 
 
 def decode_algorithmic_bytes(B: int, Hq: int, Hkv: int, L: int, D: int, include_q_o: bool = True,
-                             v_fp4: bool = False) -> int:
-    """v_fp4: V held in MXFP4 (D/2 bytes of codes per token) instead of E4M3."""
-    per_tok = D // 2 + D // 32 + (D // 2 if v_fp4 else D) + D // 32
+                             v_fp4: bool = False, k_nvfp4: bool = False) -> int:
+    """v_fp4: V held in MXFP4 (D/2 bytes of codes per token) instead of E4M3;
+    k_nvfp4: K's scales are E4M3 per 16 channels (D/16 bytes per token)."""
+    per_tok = D // 2 + (D // 16 if k_nvfp4 else D // 32) + (D // 2 if v_fp4 else D) + D // 32
     total = B * Hkv * L * per_tok
     if include_q_o:
         total += B * Hq * D * 2 + B * Hq * D * 4
     return total
 
 
-def prefill_roof_seconds(flops_qkpv: float, comp_flops: float = 0.0, pv_fp4: bool = False) -> float:
-    """pv_fp4: P V also on the MXFP4 MFMA (the full-FP4 contrast case)."""
+def prefill_roof_seconds(flops_qkpv: float, comp_flops: float = 0.0, pv_fp4: bool = False,
+                         qk_bf16: bool = False) -> float:
+    """pv_fp4: P V also on the MXFP4 MFMA (the full-FP4 contrast case);
+    qk_bf16: Q K^T on the bf16 MFMA (the NVFP4 emulation)."""
     half = flops_qkpv / 2.0
-    return half / PEAK_FP4 + half / (PEAK_FP4 if pv_fp4 else PEAK_FP8) + comp_flops / PEAK_BF16
+    return (half / (PEAK_BF16 if qk_bf16 else PEAK_FP4) + half / (PEAK_FP4 if pv_fp4 else PEAK_FP8)
+            + comp_flops / PEAK_BF16)
 
 
-def blended_peak(flops_qkpv: float, comp_flops: float = 0.0, pv_fp4: bool = False) -> float:
-    return (flops_qkpv + comp_flops) / prefill_roof_seconds(flops_qkpv, comp_flops, pv_fp4)
+def blended_peak(flops_qkpv: float, comp_flops: float = 0.0, pv_fp4: bool = False, qk_bf16: bool = False) -> float:
+    return (flops_qkpv + comp_flops) / prefill_roof_seconds(flops_qkpv, comp_flops, pv_fp4, qk_bf16)
