@@ -439,3 +439,31 @@ def test_decode_nvfp4_varlen():
                              nvfp4=(gq, gk))
     compare_o(to_np(O)[rows[:, 0], rows[:, 1]], res["O_q"], to_np(lse)[rows[:, 0], rows[:, 1]], res["lse_q"],
               "decode-nvfp4")
+
+
+# ----------------------------------------------------------------------------- contrast formats at full size
+@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8_BLOCKP, qfa.QFA_PV_FP4], ids=["blockp", "fp4"])
+def test_prefill_formats_llama16k_sampled(pv):
+    """The P/V contrast formats at the benchmarked size and launch (Q quantised in the kernel)."""
+    w = WORKLOADS["llama16k"]
+    inp = make_inputs(w, seed=0)
+    rows = sample_rows(1, w.Hq, w.S_q, 96, seed=3, must=(0, 127, 128, 4095))
+    _check_prefill(inp["q"], inp["k"], inp["v"], w.causal, w.scale, w.smooth, rows, "llama16k-pv%d" % pv,
+                   fused=True, pv=pv)
+
+
+def test_prefill_nvfp4_llama16k_sampled():
+    w = WORKLOADS["llama16k"]
+    inp = make_inputs(w, seed=0)
+    rows = sample_rows(1, w.Hq, w.S_q, 96, seed=4, must=(0, 127, 128, 4095))
+    _check_prefill_nv(inp["q"], inp["k"], inp["v"], w.causal, w.scale, w.smooth, rows, "llama16k-nvfp4")
+
+
+@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8_BLOCKP, qfa.QFA_PV_FP4], ids=["blockp", "fp4"])
+def test_decode_formats_workload_sampled(pv):
+    """The P/V contrast formats on the B64 x 32768 decode workload, 16 splits."""
+    w = WORKLOADS["decode"]
+    inp = make_inputs(w, seed=0)
+    used = _check_decode(inp["q"], inp["k"], inp["v"], w.num_splits, label="decode-B64-pv%d" % pv, seqs=[0, 42],
+                         pv=pv)
+    assert used == 16
