@@ -10,6 +10,8 @@
 //                 with the rescale 2^(m - m_ref) riding on P's E8M0 scale
 //                                                                [pv_tile]
 // pv_then_qk runs the P V of one tile and the S^T of the next back to back.
+// Every step is templated on the kernel format: the method (above) or one of
+// the contrast formats described at pv_of below.
 // Method: "MpFA: Hardware-Efficient Train-Free QK4V8 FlashAttention Kernels on
 // Blackwell GPUs" (abstract); online softmax per the FP4 tutorial
 // "FlashAttention压到4位", section "注意力慢在哪儿"; the denominator uses the
@@ -22,14 +24,7 @@
 
 namespace qfa {
 
-// LDS image of one K/V tile (128 keys):
-//   K region [K codes 128 x D/2][K scales, 1 KB area]
-//   V region [V codes 4 x D x VR][V scales, 1 KB area]  (VR = 32 bytes per
-//            (32-token block, channel) record in E4M3, 16 in MXFP4)
-// The two regions may live in separate buffers (KREG / VREG bytes each).
-// K and V codes are stored with an XOR swizzle of their 16-byte chunks (see
-// kswz / vswz) so that the MFMA operand reads are free of bank conflicts.
-// P/V formats.  PV_FP8 is the method: P = E4M3(256 * 2^(y - m)) with one
+// Kernel formats.  PV_FP8 is the method: P = E4M3(256 * 2^(y - m)) with one
 // power-of-two scale per row (the running max m) and V in E4M3.
 // PV_FP8_BLOCKP gives P one E8M0 scale per (row, 32 keys): block b is coded
 // as E4M3(256 * 2^(y - e_b)) with e_b = max(ceil(max_{j in b} y_j), m - 64)
@@ -52,6 +47,14 @@ constexpr int pv_of(int fmt) { return fmt == QK_NVFP4 ? PV_FP8 : fmt; }
 template <int PV>
 constexpr int v_record() { return PV == PV_FP4 ? 16 : 32; }
 
+// LDS image of one K/V tile (128 keys):
+//   K region [K codes 128 x D/2][K scales, 1 KB area]
+//   V region [V codes 4 x D x VR][V scales, 1 KB area]  (VR = 32 bytes per
+//            (32-token block, channel) record in E4M3, 16 in MXFP4)
+// The two regions may live in separate buffers (KREG / VREG bytes each).
+// K codes and E4M3 V records are stored with an XOR swizzle of their 16-byte
+// chunks (see kswz / vswz) so that the MFMA operand reads are free of bank
+// conflicts; an MXFP4 V record is one 16-byte chunk and needs none.
 template <int D, int PV = PV_FP8>
 struct TileLayout {
   static constexpr int KC = kTile * D / 2;
