@@ -37,7 +37,7 @@ EXPORTS = (
     "qfa_quantize_qk4", "qfa_quantize_v8", "qfa_fwd_prefill", "qfa_fwd_decode",
     "qfa_decode_workspace_bytes", "qfa_decode_default_splits", "qfa_exp2_scale", "qfa_kv_append",
     "qfa_fwd_prefill_ex", "qfa_fwd_decode_ex", "qfa_quantize_v4",
-    "qfa_quantize_nvfp4", "qfa_fwd_prefill_nvfp4", "qfa_fwd_decode_nvfp4",
+    "qfa_quantize_nvfp4", "qfa_fwd_prefill_nvfp4", "qfa_fwd_decode_nvfp4", "qfa_kv_append_ex",
     "qfa_status_string", "qfa_version",
 )
 
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.qfa_decode_workspace_bytes.argtypes = [I, I, I, I]
         L.qfa_decode_default_splits.restype = I
         L.qfa_decode_default_splits.argtypes = [I, I, I]
+        L.qfa_kv_append_ex.restype = I
+        L.qfa_kv_append_ex.argtypes = [P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, F, P]
         L.qfa_kv_append.restype = I
         L.qfa_kv_append.argtypes = [P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
         L.qfa_exp2_scale.restype = F
@@ -223,6 +225,15 @@ def qfa_fwd_decode_ex(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_
     return ns.value
 
 
+def qfa_kv_append_ex(k_new, v_new, B, Hkv, n_new, D, S_kv_max, block_size, kv_lens, k4, k4s, kbar, v8, v8s,
+                     k_tail, v_tail, pv_format, k_tensor_scale, stream=None):
+    _check("qfa_kv_append_ex", lib().qfa_kv_append_ex(
+        _ptr(_u16(k_new)), _ptr(_u16(v_new)), B, Hkv, n_new, D, S_kv_max, block_size, _ptr(kv_lens), _ptr(k4),
+        _ptr(k4s), _ptr(None if kbar is None else _u16(kbar)), _ptr(v8), _ptr(v8s),
+        _ptr(None if k_tail is None else _u16(k_tail)), _ptr(_u16(v_tail)), int(pv_format), float(k_tensor_scale),
+        _stream(stream)))
+
+
 def qfa_kv_append(k_new, v_new, B, Hkv, n_new, D, S_kv_max, block_size, kv_lens, k4, k4s, kbar, v8, v8s, k_tail,
                   v_tail, stream=None):
     _check("qfa_kv_append", lib().qfa_kv_append(
@@ -232,15 +243,19 @@ def qfa_kv_append(k_new, v_new, B, Hkv, n_new, D, S_kv_max, block_size, kv_lens,
 
 
 # ----------------------------------------------------------------------------- allocating helpers
-def kv_cache(B: int, Hkv: int, S_kv_max: int, D: int, smooth: bool = False, device="cuda"):
-    """Empty pre-quantised KV cache (the layouts qfa_fwd_decode reads) plus the bf16 tails
-    qfa_kv_append keeps between calls."""
+def kv_cache(B: int, Hkv: int, S_kv_max: int, D: int, smooth: bool = False, device="cuda",
+             pv_format: int = QFA_PV_FP8, k_tensor_scale: float = 0.0):
+    """Empty pre-quantised KV cache (the layouts the decode entry points read) plus the bf16
+    tails qfa_kv_append keeps between calls.  pv_format QFA_PV_FP4: V in MXFP4;
+    k_tensor_scale > 0: K in NVFP4 with that tensor scale."""
     nvb, nt = (S_kv_max + 31) // 32, (S_kv_max + 127) // 128
     u8 = dict(dtype=torch.uint8, device=device)
-    c = {"k4": torch.zeros((B, Hkv, S_kv_max, D // 2), **u8), "k4s": torch.zeros((B, Hkv, S_kv_max, D // 32), **u8),
-         "v8": torch.zeros((B, Hkv, nvb, D, 32), **u8), "v8s": torch.zeros((B, Hkv, nvb, D), **u8),
+    ks = D // 16 if k_tensor_scale > 0 else D // 32
+    vr = 16 if pv_format == QFA_PV_FP4 else 32
+    c = {"k4": torch.zeros((B, Hkv, S_kv_max, D // 2), **u8), "k4s": torch.zeros((B, Hkv, S_kv_max, ks), **u8),
+         "v8": torch.zeros((B, Hkv, nvb, D, vr), **u8), "v8s": torch.zeros((B, Hkv, nvb, D), **u8),
          "v_tail": torch.zeros((B, Hkv, 128, D), dtype=torch.bfloat16, device=device),
-         "kbar": None, "k_tail": None, "S": S_kv_max}
+         "kbar": None, "k_tail": None, "S": S_kv_max, "pv_format": pv_format, "k_tensor_scale": k_tensor_scale}
     if smooth:
         c["kbar"] = torch.zeros((B, Hkv, nt, D), dtype=torch.bfloat16, device=device)
         c["k_tail"] = torch.zeros((B, Hkv, 128, D), dtype=torch.bfloat16, device=device)
@@ -250,8 +265,11 @@ def kv_cache(B: int, Hkv: int, S_kv_max: int, D: int, smooth: bool = False, devi
 def kv_append(cache, k_new: torch.Tensor, v_new: torch.Tensor, kv_lens=None, stream=None):
     """Append bf16 k_new, v_new [B,Hkv,n,D] at kv_lens (device int32 [B] or None = empty cache)."""
     B, Hkv, n, D = k_new.shape
-    qfa_kv_append(k_new, v_new, B, Hkv, n, D, cache["S"], 32, kv_lens, cache["k4"], cache["k4s"], cache["kbar"],
-                  cache["v8"], cache["v8s"], cache["k_tail"], cache["v_tail"], stream)
+    qfa_kv_append_ex(k_new, v_new, B, Hkv, n, D, cache["S"], 32, kv_lens, cache["k4"], cache["k4s"], cache["kbar"],
+                     cache["v8"], cache["v8s"], cache["k_tail"], cache["v_tail"], cache.get("pv_format", QFA_PV_FP8),
+                     cache.get("k_tensor_scale", 0.0), stream)
+
+
 def quantize_qk4(x: torch.Tensor, smooth: bool = False, prescale: float = 1.0, stream=None):
     """x bf16 [B,H,S,D] on the GPU -> (codes u8 [B,H,S,D/2], scales u8 [B,H,S,D/32], kbar bf16 or None).
 

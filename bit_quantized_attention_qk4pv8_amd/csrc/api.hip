@@ -191,7 +191,17 @@ qfa_status qfa_kv_append(const uint16_t* k_new, const uint16_t* v_new, int B, in
                          int S_kv_max, int block_size, const int32_t* kv_lens, uint8_t* k4, uint8_t* k4s,
                          uint16_t* kbar, uint8_t* v8, uint8_t* v8s, uint16_t* k_tail, uint16_t* v_tail,
                          hipStream_t stream) {
+  return qfa_kv_append_ex(k_new, v_new, B, Hkv, n_new, D, S_kv_max, block_size, kv_lens, k4, k4s, kbar, v8, v8s,
+                          k_tail, v_tail, QFA_PV_FP8, 0.0f, stream);
+}
+
+qfa_status qfa_kv_append_ex(const uint16_t* k_new, const uint16_t* v_new, int B, int Hkv, int n_new, int D,
+                            int S_kv_max, int block_size, const int32_t* kv_lens, uint8_t* k4, uint8_t* k4s,
+                            uint16_t* kbar, uint8_t* v8, uint8_t* v8s, uint16_t* k_tail, uint16_t* v_tail,
+                            int pv_format, float k_tensor_scale, hipStream_t stream) {
   if (block_size != 32 || !qk_dim_ok(D)) return QFA_ERR_UNSUPPORTED;
+  if (qfa_status f = check_pv_format(pv_format); f != QFA_OK) return f;
+  if (k_tensor_scale != 0.0f && !pow2_ok(k_tensor_scale)) return QFA_ERR_INVALID_ARG;
   if (B < 0 || Hkv < 0 || n_new < 0 || S_kv_max < 0 || (long long)B * Hkv > 65535) return QFA_ERR_INVALID_ARG;
   if ((kbar == nullptr) != (k_tail == nullptr)) return QFA_ERR_INVALID_ARG;
   if ((long long)B * Hkv * n_new == 0 || S_kv_max == 0) return QFA_OK;
@@ -205,6 +215,8 @@ qfa_status qfa_kv_append(const uint16_t* k_new, const uint16_t* v_new, int B, in
   a.k4 = k4; a.k4s = k4s; a.kbar = kbar; a.v8 = v8; a.v8s = v8s;
   a.k_tail = k_tail; a.v_tail = v_tail;
   a.B = B; a.Hkv = Hkv; a.n = n_new; a.S = S_kv_max;
+  a.v_fp4 = pv_format == QFA_PV_FP4;
+  a.k_nv_g = k_tensor_scale;
   return from_hip(qfa::launch_kv_append(a, D, stream));
 }
 

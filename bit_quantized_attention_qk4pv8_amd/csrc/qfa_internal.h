@@ -209,6 +209,8 @@ struct AppendArgs {
   uint16_t* k_tail;        // bf16 [B][Hkv][128][D]; null iff kbar null
   uint16_t* v_tail;        // bf16 [B][Hkv][128][D]
   int B, Hkv, n, S;
+  int v_fp4;               // V records in MXFP4 (16 bytes) instead of E4M3 (32 bytes)
+  float k_nv_g;            // > 0: K in NVFP4 with this tensor scale; 0: K in MXFP4
 };
 hipError_t launch_kv_append(const AppendArgs& a, int D, hipStream_t s);
 hipError_t launch_decode(const AttnArgs& a, float* O, float* lse, hipStream_t s);

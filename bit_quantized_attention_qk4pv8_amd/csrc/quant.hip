@@ -256,7 +256,15 @@ __global__ void __launch_bounds__(D) k_append_v(AppendArgs a) {
   for (int t = 0; t < kBlock; ++t)
     x[t] = (t < np) ? bf16_bits_to_float(tok_row<D>(a.v_tail, a.v_new, bg, a.n, L, j0 + t)[c]) : 0.0f;
   const size_t nvb = (size_t)(a.S + kBlock - 1) / kBlock;
-  fp8_block_store(x, a.v8 + ((bg * nvb + blk) * D + c) * kBlock, a.v8s + (bg * nvb + blk) * D + c);
+  if (a.v_fp4) {  // MXFP4 record of the full-FP4 cache
+    uint4 cd;
+    uint8_t sc;
+    mxfp4_block(x, cd, sc);
+    *reinterpret_cast<uint4*>(a.v8 + ((bg * nvb + blk) * D + c) * (kBlock / 2)) = cd;
+    a.v8s[(bg * nvb + blk) * D + c] = sc;
+  } else {
+    fp8_block_store(x, a.v8 + ((bg * nvb + blk) * D + c) * kBlock, a.v8s + (bg * nvb + blk) * D + c);
+  }
 }
 
 // One workgroup per (affected 128-token K tile, sequence slice): K-bar of the
@@ -286,6 +294,35 @@ __global__ void __launch_bounds__(256) k_append_k(AppendArgs a, int smooth) {
     __syncthreads();
   }
   const int nrows = t0 + np - lo;
+  if (a.k_nv_g > 0.0f) {  // NVFP4 rows (blocks of 16, E4M3 scales)
+    constexpr int NB16 = D / 16;
+    for (int w = threadIdx.x; w < nrows * NB16; w += blockDim.x) {
+      const int j = lo + w / NB16, blk = w % NB16;
+      const uint16_t* src = tok_row<D>(a.k_tail, a.k_new, bg, a.n, L, j) + blk * 16;
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 u = reinterpret_cast<const uint4*>(src)[q];
+        const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[q * 8 + 2 * k] = bf16_bits_to_float(wds[k] & 0xFFFFu);
+          v[q * 8 + 2 * k + 1] = bf16_bits_to_float(wds[k] >> 16);
+        }
+      }
+      if (smooth) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = v[i] - kb[blk * 16 + i];
+      }
+      uint2 out;
+      uint8_t sc;
+      nvfp4_block(v, a.k_nv_g, out, sc);
+      const size_t row = bg * (size_t)a.S + j;
+      *reinterpret_cast<uint2*>(a.k4 + row * (D / 2) + blk * 8) = out;
+      a.k4s[row * NB16 + blk] = sc;
+    }
+    return;
+  }
   for (int w = threadIdx.x; w < nrows * NB; w += blockDim.x) {
     const int j = lo + w / NB, blk = w % NB;
     float v[kBlock];

@@ -266,6 +266,21 @@ qfa_status qfa_fwd_decode_nvfp4(const uint8_t* q4, const uint8_t* q4s, const uin
                                 float softmax_scale, float q_tensor_scale, float k_tensor_scale, int* num_splits,
                                 void* workspace, size_t workspace_bytes, float* O, float* lse, hipStream_t stream);
 
+/*
+ * qfa_kv_append for the caches of the contrast formats: pv_format QFA_PV_FP4
+ * keeps V in MXFP4 (records and scales as written by qfa_quantize_v4; the
+ * other formats keep E4M3 V), and k_tensor_scale > 0 (a power of two) keeps K
+ * in NVFP4 with that tensor scale (codes [..][D/2], E4M3 scales [..][D/16], as
+ * qfa_quantize_nvfp4 writes them; 0 keeps MXFP4 K).  The contract is the one
+ * of qfa_kv_append: afterwards the cache holds the bytes the matching
+ * quantisers write for the whole sequence at once.  qfa_kv_append is
+ * pv_format = QFA_PV_FP8, k_tensor_scale = 0.
+ */
+qfa_status qfa_kv_append_ex(const uint16_t* k_new, const uint16_t* v_new, int B, int Hkv, int n_new, int D,
+                            int S_kv_max, int block_size, const int32_t* kv_lens, uint8_t* k4, uint8_t* k4s,
+                            uint16_t* kbar, uint8_t* v8, uint8_t* v8s, uint16_t* k_tail, uint16_t* v_tail,
+                            int pv_format, float k_tensor_scale, hipStream_t stream);
+
 /* Bytes of decode workspace for the given shape and split count (> 0). */
 size_t qfa_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 

@@ -189,6 +189,13 @@ def test_kv_append_validation():
     assert app(knew=odd) == qfa.QFA_ERR_INVALID_ARG           # misaligned input
     assert app(vtail=None) == qfa.QFA_ERR_INVALID_ARG         # the V tail is always needed
     assert app(n=0, knew=None) == qfa.QFA_OK                  # nothing to append
+    F = ctypes.c_float
+    appx = lambda fmt=0, g=0.0: _call_raw(
+        "qfa_kv_append_ex", fake, fake, 2, 2, 4, 128, 1024, 32, None, fake, fake, None, fake, fake, None, fake, fmt,
+        F(g), None)
+    assert appx(fmt=7) == qfa.QFA_ERR_INVALID_ARG             # unknown V format
+    assert appx(g=3.0) == qfa.QFA_ERR_INVALID_ARG             # the NVFP4 tensor scale is a power of two
+    assert appx(g=-1.0) == qfa.QFA_ERR_INVALID_ARG
 
 
 def test_kv_cache_byte_formula_matches_printed_example():

@@ -105,3 +105,81 @@ def test_append_matches_oracle_and_feeds_decode():
     O2, l2, _ = qfa.fwd_decode(None, None, k4, k4s, v8, v8s, L, 1 / math.sqrt(D), num_splits=3, kbar=kb, q_bf16=q)
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(l1, l2)
+
+
+def _check_formats_one_shot(c, k, v, lens, smooth, pv, g, label):
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        ks = k[b:b + 1, :, :L].contiguous()
+        if g > 0:
+            k4, k4s, kb = qfa.quantize_nvfp4(ks, g, smooth=smooth)
+        else:
+            k4, k4s, kb = qfa.quantize_qk4(ks, smooth=smooth)
+        vs = v[b:b + 1, :, :L].contiguous()
+        v8, v8s = qfa.quantize_v4(vs) if pv == qfa.QFA_PV_FP4 else qfa.quantize_v8(vs)
+        nvb, nt = (L + 31) // 32, (L + 127) // 128
+        assert torch.equal(c["k4"][b:b + 1, :, :L], k4), (label, b, "K codes")
+        assert torch.equal(c["k4s"][b:b + 1, :, :L], k4s), (label, b, "K scales")
+        assert torch.equal(c["v8"][b:b + 1, :, :nvb], v8), (label, b, "V codes")
+        assert torch.equal(c["v8s"][b:b + 1, :, :nvb], v8s), (label, b, "V scales")
+        if smooth:
+            assert torch.equal(c["kbar"][b:b + 1, :, :nt], kb), (label, b, "K-bar")
+
+
+@pytest.mark.parametrize("pv,nv,smooth", [(qfa.QFA_PV_FP4, False, True), (qfa.QFA_PV_FP4, False, False),
+                                          (qfa.QFA_PV_FP8, True, True), (qfa.QFA_PV_FP8, True, False)],
+                         ids=["v4-smooth", "v4", "nvfp4k-smooth", "nvfp4k"])
+def test_append_formats_in_chunks_equals_one_shot(pv, nv, smooth):
+    """The cache writer for the contrast formats (MXFP4 V, NVFP4 K): chunked
+    appends leave the bytes of the one-shot quantisers of that format, and the
+    format's decode reads the appended cache (checked against the oracle
+    without smoothing)."""
+    B, Hkv, S, D = 3, 2, 700, 128
+    k, v = _data(B, Hkv, S, D, seed=11 + pv + 2 * nv + 4 * smooth)
+    g = qfa.nvfp4_tensor_scale(float(k.float().abs().max())) if nv else 0.0
+    c = qfa.kv_cache(B, Hkv, S, D, smooth=smooth, pv_format=pv, k_tensor_scale=g)
+    lens = [0, 5, 200]
+    for b, L0 in enumerate(lens):
+        if L0:
+            qfa.kv_append(_sl(c, b), k[b:b + 1, :, :L0].contiguous(), v[b:b + 1, :, :L0].contiguous())
+    for n in (1, 31, 33, 130, 97):
+        say("kv_append formats pv", pv, "nvfp4 K", nv, "smooth", smooth, "lens", lens, "n", n)
+        kl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        kn = torch.stack([k[b, :, lens[b]:lens[b] + n] for b in range(B)]).contiguous()
+        vn = torch.stack([v[b, :, lens[b]:lens[b] + n] for b in range(B)]).contiguous()
+        qfa.kv_append(c, kn, vn, kv_lens=kl)
+        torch.cuda.synchronize()
+        lens = [L + n for L in lens]
+        _check_formats_one_shot(c, k, v, lens, smooth, pv, g, "after +%d" % n)
+    Hq = 8
+    q = torch.randn((B, Hq, 1, D), device="cuda").to(torch.bfloat16)
+    kl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    scale = 1 / math.sqrt(D)
+    say("decode on the appended cache, lens", lens)
+    if nv:
+        c2 = qfa.qfa_exp2_scale(scale)
+        gq = qfa.nvfp4_tensor_scale(float((q.float() * c2).abs().max()))
+        q4, q4s, _ = qfa.quantize_nvfp4(q, gq, prescale=c2)
+        wsb = qfa.qfa_decode_workspace_bytes(B, Hq, D, 3)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        O = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        qfa.qfa_fwd_decode_nvfp4(q4, q4s, c["k4"], c["k4s"], c["kbar"], q if smooth else None, c["v8"], c["v8s"],
+                                 B, Hq, Hkv, S, kl, D, scale, gq, g, 3, ws, wsb, O, lse)
+    else:
+        O, lse, _ = qfa.fwd_decode(None, None, c["k4"], c["k4s"], c["v8"], c["v8s"], S, scale, num_splits=3,
+                                   kv_lens=kl, kbar=c["kbar"], q_bf16=q, pv_format=pv)
+    torch.cuda.synchronize()
+    assert torch.isfinite(O).all()
+    if not smooth:
+        rows = np.array([(b, h, 0) for b in range(B) for h in range(Hq)], dtype=np.int64)
+        full_k = torch.zeros((B, Hkv, S, D), dtype=torch.bfloat16, device="cuda")
+        full_v = torch.zeros_like(full_k)
+        for b, L in enumerate(lens):
+            full_k[b, :, :L], full_v[b, :, :L] = k[b, :, :L], v[b, :, :L]
+        res = oracle.decode_rows(bf16_bits(q), bf16_bits(full_k), bf16_bits(full_v), rows, scale, 3, kv_lens=lens,
+                                 pv=oracle.PV_FP4 if pv == qfa.QFA_PV_FP4 else oracle.PV_FP8,
+                                 nvfp4=(gq, g) if nv else None, exact=False)
+        Og = to_np(O)[rows[:, 0], rows[:, 1]]
+        assert np.abs(Og - res["O_q"]).max() < 3e-3
