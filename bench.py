@@ -105,7 +105,7 @@ def traffic_from_profile(name, src_hash):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(each GPU would run its own shard with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.only == "copy":
