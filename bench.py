@@ -184,7 +184,7 @@ def main():
                        "step": "quantize K (MXFP4) + V (FP8), then the prefill kernel with Q quantised in-kernel"},
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 2), "unit": "TFLOP/s",
                          "frac": round(achieved / peak, 4), "traffic": traffic,
-                         "kernel": "qfa::k_prefill<128,%s,0>" % ("true" if w.smooth else "false"),
+                         "kernel": "qfa::k_prefill<%d,%s,0>" % (D, "true" if w.smooth else "false"),
                          "kernel_ms": round(kern_ms, 4), "algorithmic_flop_per_launch": flops + comp},
         })
         if not args.no_variants and args.only == "all":
@@ -210,7 +210,7 @@ def main():
                 out["variants"][name] = {
                     "prefill": {"kernel_ms": round(vk, 4), "achieved": round(vach, 2), "peak": round(vpeak, 2),
                                 "unit": "TFLOP/s", "frac": round(vach / vpeak, 4),
-                                "kernel": "qfa::k_prefill<128,%s,%d>" % ("true" if w.smooth else "false", pv)}}
+                                "kernel": "qfa::k_prefill<%d,%s,%d>" % (D, "true" if w.smooth else "false", pv)}}
                 del vq, vqs
             # NVFP4 Q and K (emulated on the bf16 MFMA), P and V as in the method
             c2 = qfa.qfa_exp2_scale(w.scale)
@@ -236,7 +236,7 @@ def main():
             out["variants"]["nvfp4_qk"] = {
                 "prefill": {"kernel_ms": round(vk, 4), "achieved": round(vach, 2), "peak": round(vpeak, 2),
                             "unit": "TFLOP/s", "frac": round(vach / vpeak, 4),
-                            "kernel": "qfa::k_prefill<128,%s,3>" % ("true" if w.smooth else "false"),
+                            "kernel": "qfa::k_prefill<%d,%s,3>" % (D, "true" if w.smooth else "false"),
                             "note": "Q K^T emulated on the bf16 MFMA; peak counts it at bf16"}}
             del q4n, q4ns, k4n, k4ns, kbn
         del O, lse
