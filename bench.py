@@ -44,8 +44,10 @@ sys.path.insert(0, ROOT)
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=10)
+    # 100 untimed steps (about 0.1 s of GPU work per half) bring the clocks to
+    # steady state: after 10 the prefill kernel still ran 5-6% slower
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-variants", action="store_true")

@@ -256,9 +256,17 @@ def test_decode_compensation():
 def test_decode_workload_sampled_sequences():
     w = WORKLOADS["decode"]
     inp = make_inputs(w, seed=0)
-    used = _check_decode(inp["q"], inp["k"], inp["v"], w.num_splits, label="decode-B64",
-                         seqs=[0, 17, 42, 63])
+    seqs = [0, 17, 42, 63]
+    used = _check_decode(inp["q"], inp["k"], inp["v"], w.num_splits, label="decode-B64", seqs=seqs)
     assert used == 16
+    # error of the method against exact FP64 attention on the same rows (reported, not gated)
+    O, _, _ = _gpu_decode(inp["q"], inp["k"], inp["v"], w.num_splits)
+    rows = np.array([(b, h, 0) for b in seqs for h in range(w.Hq)], dtype=np.int64)
+    ex = oracle.prefill_rows(bf16_bits(inp["q"]), bf16_bits(inp["k"]), bf16_bits(inp["v"]), rows, False, w.scale)
+    Og = to_np(O)[rows[:, 0], rows[:, 1]]
+    err = np.linalg.norm(Og - ex["O_x"]) / np.linalg.norm(ex["O_x"])
+    cos = float(np.sum(Og * ex["O_x"]) / (np.linalg.norm(Og) * np.linalg.norm(ex["O_x"])))
+    say("decode-B64 vs exact FP64: rel-L2 %.3e cosine %.6f (reported only)" % (err, cos))
 
 
 @pytest.mark.parametrize("smooth", [False, True])
