@@ -88,6 +88,9 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
 }
 
 // LSE merge: one wave per (b, h) row.  LSE = log sum_s e^{LSE_s};  O = sum_s e^{LSE_s - LSE} O_s.
+// Lane s holds split s's LSE and weight (64 splits per pass, broadcast by
+// readlane); the partial-O loads of eight splits are issued together, so
+// their latencies overlap.
 template <int D>
 __global__ void __launch_bounds__(256) k_decode_merge(const float* __restrict__ Op, const float* __restrict__ Lp,
                                                       int rows, int S, float* __restrict__ O, float* __restrict__ lse) {
@@ -95,20 +98,43 @@ __global__ void __launch_bounds__(256) k_decode_merge(const float* __restrict__ 
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float* lp = Lp + (size_t)row * S;
+  const float* op = Op + (size_t)row * S * D;
   float mx = -__builtin_inff();
-  for (int s = 0; s < S; ++s) mx = __builtin_fmaxf(mx, lp[s]);
+  for (int s0 = 0; s0 < S; s0 += 64)
+    if (s0 + lane < S) mx = __builtin_fmaxf(mx, lp[s0 + lane]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
   float acc[D / 64];
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) acc[k] = 0.0f;
   float den = 0.0f;
   if (mx != -__builtin_inff()) {
-    for (int s = 0; s < S; ++s) {
-      const float w = __expf(lp[s] - mx);
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int ns = min(64, S - s0);
+      const float w = lane < ns ? __expf(lp[s0 + lane] - mx) : 0.0f;
       den += w;
-      const float* op = Op + ((size_t)row * S + s) * D;
+      int s = 0;
+      for (; s + 8 <= ns; s += 8) {
+        float v[8][D / 64], ws[8];
 #pragma unroll
-      for (int k = 0; k < D / 64; ++k) acc[k] += w * op[64 * k + lane];
+        for (int j = 0; j < 8; ++j) {
+          ws[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + j));
+#pragma unroll
+          for (int k = 0; k < D / 64; ++k) v[j][k] = op[(size_t)(s0 + s + j) * D + 64 * k + lane];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int k = 0; k < D / 64; ++k) acc[k] += ws[j] * v[j][k];
+      }
+      for (; s < ns; ++s) {
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) acc[k] += ws * op[(size_t)(s0 + s) * D + 64 * k + lane];
+      }
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
   }
   const float inv = (den > 0.0f) ? 1.0f / den : 0.0f;
 #pragma unroll
