@@ -2,7 +2,7 @@
 """Benchmark of the QK4PV8 attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only all|prefill|decode|copy]
+                    [--only all|prefill|decode|copy|stream]
 
 One step = the whole prefill hot path over the Llama-3.1-8B-shaped workload
 (B1, Hq32/Hkv8, S16384, D128, causal; bf16 inputs resident in HBM): quantise K
@@ -27,7 +27,8 @@ emulated on, each decode against its own cache bytes).
 `--only prefill|decode` runs just that half (for hardware-counter passes);
 `--only copy` runs a plain device-to-device copy of 1 GiB, the reference
 kernel of known size that scales the FETCH_SIZE / WRITE_SIZE counters into
-bytes.
+bytes; `--only stream` times a 4 GiB row-wise device sum, the read-bandwidth
+ceiling quoted beside the decode.
 """
 import argparse
 import hashlib
@@ -52,13 +53,38 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-variants", action="store_true")
     p.add_argument("--workload", default="llama16k")
-    p.add_argument("--only", default="all", choices=("all", "prefill", "decode", "copy"))
+    p.add_argument("--only", default="all", choices=("all", "prefill", "decode", "copy", "stream"))
     return p.parse_args()
 
 
 COPY_BYTES = 1 << 30
 CPU_TARGET_S = 15.0
 MAX_CPU_ROWS = 131072  # bounded CPU sample: at most a quarter of llama16k's 524288 rows
+
+
+STREAM_BYTES = 4 << 30
+
+
+def run_stream(args):
+    """Device read bandwidth: 4 GiB reduced row by row (rows of 16 KB, a 1 MiB
+    result), timed like the attention kernels.  The ceiling that a streaming
+    kernel such as the split-KV decode can approach (reported beside the
+    decode's fraction of the 8 TB/s peak, not graded).  A full reduction to
+    one scalar reads at only about 4 TB/s, so it would understate this."""
+    import torch
+    x = torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device="cuda:0").view(-1, 4096)
+    for _ in range(args.warmup):
+        x.sum(dim=1)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        x.sum(dim=1)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"stream_bytes_read": STREAM_BYTES, "ms": round(ms, 4),
+                      "GB/s": round(STREAM_BYTES / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def run_copy(args):
@@ -112,6 +138,9 @@ def main():
         sys.exit(2)
     if args.only == "copy":
         run_copy(args)
+        return
+    if args.only == "stream":
+        run_stream(args)
         return
 
     import numpy as np
