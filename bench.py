@@ -65,6 +65,24 @@ MAX_CPU_ROWS = 131072  # bounded CPU sample: at most a quarter of llama16k's 524
 STREAM_BYTES = 4 << 30
 
 
+def stream_read_gbs(warmup=20, steps=50):
+    """GB/s of the row-wise 4 GiB sum (see run_stream)."""
+    import torch
+    x = torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device="cuda:0").view(-1, 4096)
+    for _ in range(warmup):
+        x.sum(dim=1)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        x.sum(dim=1)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    del x
+    return STREAM_BYTES / (ms * 1e-3) / 1e9
+
+
 def run_stream(args):
     """Device read bandwidth: 4 GiB reduced row by row (rows of 16 KB, a 1 MiB
     result), timed like the attention kernels.  The ceiling that a streaming
@@ -320,6 +338,10 @@ def main():
                          "kernel": "qfa::k_decode_split<128,false,0> + k_decode_merge<128>",
                          "algorithmic_bytes_per_launch": dbytes},
         }
+        # context, not graded: the device's measured read bandwidth
+        ceil_gbs = stream_read_gbs()
+        out["decode"]["stream_read_ceiling"] = {"GB/s": round(ceil_gbs, 1), "frac": round(gbs / ceil_gbs, 4),
+                                                "kernel": "row-wise sum of 4 GiB (torch)"}
         if not args.no_variants and args.only == "all":
             vd = make_inputs(wd, seed=0, device=dev)["v"]
             for name, pv in (("qk4pv8_blockp", qfa.QFA_PV_FP8_BLOCKP), ("qk4pv4", qfa.QFA_PV_FP4)):
