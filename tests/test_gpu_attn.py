@@ -248,6 +248,14 @@ def test_decode_d64_and_more_splits_than_tiles():
     _check_decode(q, k, v, 7, label="d64-7splits")   # 3 tiles: splits 3..6 are empty
 
 
+def test_decode_more_than_64_splits():
+    """The LSE merge takes split weights 64 lanes at a time: 70 splits of 9000 keys
+    (71 tiles) run a full chunk and a partial one."""
+    q, k, v = _rand_inputs(1, 4, 1, 1, 9000, 128, seed=14)
+    used = _check_decode(q, k, v, 70, label="decode-70splits")
+    assert used == 70
+
+
 def test_decode_compensation():
     q, k, v = _rand_inputs(2, 4, 1, 1, 5000, 128, seed=13, k_offset=3.0)
     _check_decode(q, k, v, 2, label="decode-comp", smooth=True)
