@@ -43,11 +43,11 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
   load_q<D, PV>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * TileLayout<D, PV>::KSB : nullptr,
                 a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid, a.nv_gq, a.nv_gk);
 
+  // (no zeroing of the tile buffers: every byte a tile step reads is written by
+  // that tile's DMA first, and the DMA writes zeros for the lanes its range
+  // check cuts off -- measured on MI355X -- so a ragged tile reads zeros)
   uint8_t* bufs = smem;
   float* dl = reinterpret_cast<float*>(smem + 2 * TL::STRIDE);
-  for (int o = threadIdx.x * 16; o < 2 * TL::STRIDE; o += blockDim.x * 16)
-    *reinterpret_cast<uint4*>(bufs + o) = make_uint4(0u, 0u, 0u, 0u);
-  __syncthreads();
   TileLoader<D, 1, PV> ld;
   ld.init(a.k4, a.k4s, a.v8, a.v8s, (size_t)bg, Lmax, L, 0);
   LaneOffs<D, PV> lo;
