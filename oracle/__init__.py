@@ -44,14 +44,23 @@ PV_FP8, PV_FP8_BLOCKP, PV_FP4 = 0, 1, 2
 _P_MODE_OF_PV = {PV_FP8: P_E4M3, PV_FP8_BLOCKP: P_E4M3_BLOCK, PV_FP4: P_E2M1_BLOCK}
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (plain C11, OpenMP)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-std=gnu11", "-O2", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+# -ffp-contract=off: every operation rounds as written (no fused multiply-add
+# contraction), so the binary32 and binary64 steps are the ones stated in
+# qfa_oracle.c.  x86-64-v3 (AVX2, FMA) runs on any current x86 server host.
+CFLAGS = ["-std=gnu11", "-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared"]
+
+
+def build(force: bool = False, out: Optional[str] = None, march: Optional[str] = None) -> str:
+    """Compile the oracle with gcc (plain C11, OpenMP).  out/march build a
+    separate copy (e.g. -march=native for timing on the host that runs it)."""
+    target = out or _LIB
+    if force or out or not os.path.exists(target) or os.path.getmtime(target) < os.path.getmtime(_SRC):
+        tmp = target + ".tmp%d" % os.getpid()
+        flags = [f if not (march and f.startswith("-march=")) else "-march=" + march for f in CFLAGS]
+        cmd = ["gcc"] + flags + [_SRC, "-o", tmp, "-lm"]
         subprocess.check_call(cmd)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, target)
+    return target
 
 
 def lib():
