@@ -213,3 +213,15 @@ def test_kv_cache_byte_formula_matches_printed_example():
     # QK4 / V8 with E8M0 scales: 64 + 4 + 128 + 4 = 200 bytes per token per kv head at D = 128
     assert decode_algorithmic_bytes(B=1, Hq=1, Hkv=1, L=1, D=128, include_q_o=False) == 200
     assert decode_algorithmic_bytes(B=64, Hq=32, Hkv=8, L=32768, D=128) == 3357016064
+
+
+def test_probe_library_loads_and_exports_its_symbols():
+    """The test-only HIP library of GPU-side pins (tests/hip) is built and
+    resolves every symbol; it is separate from libqfa."""
+    import sys
+    sys.path.insert(0, os.path.join(ROOT, "tests", "hip"))
+    import build_probe
+    L = build_probe.load()
+    for name in build_probe.SYMBOLS:
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value, name
+    assert not any(hasattr(qfa.lib(), name) for name in build_probe.SYMBOLS)
