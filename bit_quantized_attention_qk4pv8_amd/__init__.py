@@ -38,8 +38,11 @@ EXPORTS = (
     "qfa_decode_workspace_bytes", "qfa_decode_default_splits", "qfa_exp2_scale", "qfa_kv_append",
     "qfa_fwd_prefill_ex", "qfa_fwd_decode_ex", "qfa_quantize_v4",
     "qfa_quantize_nvfp4", "qfa_fwd_prefill_nvfp4", "qfa_fwd_decode_nvfp4", "qfa_kv_append_ex",
-    "qfa_status_string", "qfa_version",
+    "qfa_status_string", "qfa_version", "qfa_fwd_decode_noalloc",
 )
+
+# Capacity of the library-owned decode scratch of qfa_fwd_decode_noalloc (include/qfa.h)
+QFA_DECODE_NOALLOC_MAX_BYTES = 32 << 20
 
 _lib = None
 
@@ -76,6 +79,9 @@ def lib() -> ctypes.CDLL:
         L.qfa_fwd_decode.restype = I
         L.qfa_fwd_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P, I, F, I, ctypes.POINTER(I), P, SZ, P,
                                      P, P]
+        L.qfa_fwd_decode_noalloc.restype = I
+        L.qfa_fwd_decode_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P, I, F, I, ctypes.POINTER(I), P,
+                                             P, P]
         L.qfa_fwd_prefill_ex.restype = I
         L.qfa_fwd_prefill_ex.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P]
         L.qfa_fwd_decode_ex.restype = I
@@ -203,6 +209,16 @@ def qfa_fwd_decode(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max
         _ptr(None if q_bf16 is None else _u16(q_bf16)), _ptr(v8), _ptr(v8s), B, Hq, Hkv, S_kv_max,
         _ptr(kv_lens), D, float(softmax_scale), block_size, ctypes.byref(ns), _ptr(workspace),
         int(workspace_bytes), _ptr(O), _ptr(lse), _stream(stream)))
+    return ns.value
+
+
+def qfa_fwd_decode_noalloc(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D,
+                           softmax_scale, block_size, num_splits, O, lse, stream=None) -> int:
+    ns = ctypes.c_int(int(num_splits))
+    _check("qfa_fwd_decode_noalloc", lib().qfa_fwd_decode_noalloc(
+        _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(None if kbar is None else _u16(kbar)),
+        _ptr(None if q_bf16 is None else _u16(q_bf16)), _ptr(v8), _ptr(v8s), B, Hq, Hkv, S_kv_max,
+        _ptr(kv_lens), D, float(softmax_scale), block_size, ctypes.byref(ns), _ptr(O), _ptr(lse), _stream(stream)))
     return ns.value
 
 

@@ -3,8 +3,15 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/qfa.h"
 #include "qfa_internal.h"
+
+// Decode partials of qfa_fwd_decode_noalloc: one array per GPU, kept until the
+// process ends.  In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress (scratch_on_current_device).
+static __device__ __align__(256) uint8_t scratch[QFA_DECODE_NOALLOC_MAX_BYTES];
 
 namespace {
 
@@ -26,6 +33,26 @@ size_t ws_bytes(int B, int Hq, int D, int splits) {
   size_t o = rows * D * sizeof(float);
   o = (o + 255) / 256 * 256;
   return o + (rows * sizeof(float) + 255) / 256 * 256;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, resolved once
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with that device current).
+qfa_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QFA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return QFA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QFA_OK;
 }
 
 }  // namespace
@@ -280,6 +307,29 @@ static qfa_status decode_common(const uint8_t* q4, const uint8_t* q4s, const uin
   a.nv_gq = gq;
   a.nv_gk = gk;
   return from_hip(qfa::launch_decode(a, O, lse, stream));
+}
+
+qfa_status qfa_fwd_decode_noalloc(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                                  const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8,
+                                  const uint8_t* v8s, int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens,
+                                  int D, float softmax_scale, int block_size, int* num_splits, float* O, float* lse,
+                                  hipStream_t stream) {
+  // host checks first: a call that is rejected makes no HIP call at all
+  if (!num_splits || S_kv_max < 0 || *num_splits < 0 || *num_splits > 4096) return QFA_ERR_INVALID_ARG;
+  qfa_status st = check_attn_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, D, softmax_scale,
+                                    block_size, O);
+  if (st != QFA_OK) return st;
+  if (B == 0)
+    return decode_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D, softmax_scale,
+                         block_size, QFA_PV_FP8, 1.0f, 1.0f, num_splits, nullptr, 0, O, lse, stream);
+  const int splits = *num_splits == 0 ? qfa_decode_default_splits(B, Hkv, S_kv_max) : *num_splits;
+  if (ws_bytes(B, Hq, D, splits) > (size_t)QFA_DECODE_NOALLOC_MAX_BYTES) return QFA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != QFA_OK) return st;
+  return decode_common(q4, q4s, k4, k4s, kbar, q_bf16, v8, v8s, B, Hq, Hkv, S_kv_max, kv_lens, D, softmax_scale,
+                       block_size, QFA_PV_FP8, 1.0f, 1.0f, num_splits, ws, (size_t)QFA_DECODE_NOALLOC_MAX_BYTES, O,
+                       lse, stream);
 }
 
 qfa_status qfa_fwd_decode_ex(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,

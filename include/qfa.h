@@ -172,6 +172,31 @@ qfa_status qfa_fwd_decode(const uint8_t* q4, const uint8_t* q4s, const uint8_t* 
                           size_t workspace_bytes, float* O, float* lse, hipStream_t stream);
 
 /*
+ * qfa_fwd_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * qfa_fwd_decode (P/V format QFA_PV_FP8).  The split partials go to a
+ * library-owned device array of QFA_DECODE_NOALLOC_MAX_BYTES per GPU, created
+ * with the library's code object on each device and held until the process
+ * ends; the call itself allocates and frees nothing.  Its address is looked
+ * up once per device, on the first call made with that device current (the
+ * current device must be the one `stream` belongs to).
+ *   - A shape whose partials need more than QFA_DECODE_NOALLOC_MAX_BYTES
+ *     (qfa_decode_workspace_bytes(B, Hq, D, splits) with the split count
+ *     used) is rejected with QFA_ERR_WORKSPACE before anything is launched.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (concurrent streams, or host threads) race and must be
+ *     serialised by the caller.  No contents carry over between calls: every
+ *     partial is written before it is read.
+ */
+#define QFA_DECODE_NOALLOC_MAX_BYTES (32u << 20)
+qfa_status qfa_fwd_decode_noalloc(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s,
+                                  const uint16_t* kbar, const uint16_t* q_bf16, const uint8_t* v8,
+                                  const uint8_t* v8s, int B, int Hq, int Hkv, int S_kv_max, const int32_t* kv_lens,
+                                  int D, float softmax_scale, int block_size, int* num_splits, float* O, float* lse,
+                                  hipStream_t stream);
+
+/*
  * P/V formats.  QFA_PV_FP8 is the method described above.  The other two are
  * contrast cases: the MpFA abstract sets QK4PV8 against fully FP4 attention,
  * and the FP4 tutorial's "Direct-P" section gives P one E8M0 power-of-two
