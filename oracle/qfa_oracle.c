@@ -96,6 +96,9 @@ double orc_e2m1_value(int code) {
 int orc_e2m1_encode(double v) {
   int sign = signbit(v) ? 8 : 0;
   double a = fabs(v);
+  /* above the largest value 6 the nearest value is 6 (saturation); taken
+   * first, because for huge a every distance a - value rounds to a itself */
+  if (a > 6.0) return sign | 7;
   int best = 0;
   double bestd = INFINITY;
   for (int c = 0; c < 8; ++c) {

@@ -66,6 +66,17 @@ def test_e2m1_encode_bruteforce_and_midpoints():
     assert oracle.e2m1_encode(-0.1) == 8  # sign of zero kept
 
 
+def test_e2m1_saturates_at_every_magnitude():
+    """Every magnitude above the largest E2M1 value 6 encodes to 6 (code 7,
+    sign in bit 3), up to the largest binary64 values and infinity."""
+    for k in range(3, 1024):
+        for m in (1.0, 1.5, 1.9999999):
+            assert oracle.e2m1_encode(m * 2.0 ** k) == 7, (m, k)
+            assert oracle.e2m1_encode(-m * 2.0 ** k) == 15, (m, k)
+    assert oracle.e2m1_encode(math.inf) == 7 and oracle.e2m1_encode(-math.inf) == 15
+    assert oracle.e2m1_encode(6.000001) == 7 and oracle.e2m1_encode(5.0) == 6  # 5 is the tie 4|6 -> even (4)
+
+
 def test_e2m1_monotone():
     xs = np.linspace(-7, 7, 20001)
     vals = [oracle.e2m1_value(oracle.e2m1_encode(x)) for x in xs]
