@@ -63,11 +63,23 @@ def build(force: bool = False, out: Optional[str] = None, march: Optional[str] =
     return target
 
 
+_active = None  # path of a separately built copy in use (use_library), else the in-tree build
+
+
+def use_library(path: str) -> None:
+    """Load the oracle from another build of the same source (e.g. one built
+    with -march=native on the host that times it) from here on."""
+    global _lib, _active
+    _active = path
+    _lib = None
+
+
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB)
+        if _active is None:
+            build()
+        L = ctypes.CDLL(_active or _LIB)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         I = ctypes.c_int
@@ -418,6 +430,34 @@ def prefill_rows(q_bits, k_bits, v_bits, rows: Sequence, causal: bool, softmax_s
                                      softmax_scale)
             out["O_x"][idx] = Ox
             out["lse_x"][idx] = lx
+    return out
+
+
+def prefill_rows_from_codes(q4, q4s, k4, k4s, v8, v8s, rows: Sequence, causal: bool, softmax_scale: float,
+                            q_bits=None, kbar_bits=None) -> dict:
+    """(c) for the listed rows (b, h, i) of tensors the oracle has already
+    quantised (quantize_qk4 of Q with prescale exp2_scale(softmax_scale), of K,
+    and quantize_v8 of V); q_bits and kbar_bits (bf16) give the compensation
+    term when K was smoothed.  Decodes each KV head and the rows' Q, then runs
+    the online schedule.  Returns O_q, lse_q."""
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    B, Hq, Sq, Dh = q4.shape
+    D = 2 * Dh
+    Hkv, Skv = k4.shape[1], k4.shape[2]
+    n = rows.shape[0]
+    out = {"O_q": np.zeros((n, D)), "lse_q": np.zeros(n)}
+    for (b, g), idx in _rows_by_group(rows, Hq, Hkv).items():
+        idx = np.asarray(idx)
+        r = rows[idx]
+        Kd = dequant_qk4(k4[b, g], k4s[b, g])
+        Vd = dequant_v8(v8[b, g], v8s[b, g], Skv)
+        Qd = dequant_qk4(q4[b][r[:, 1], r[:, 2]], q4s[b][r[:, 1], r[:, 2]])
+        smooth = kbar_bits is not None
+        Qc = bf16_to_f64(q_bits[b][r[:, 1], r[:, 2]]) if smooth else None
+        Kbar = bf16_to_f64(kbar_bits[b, g]) if smooth else None
+        O, lse = attn_quant_rows(Qd, r[:, 2], Kd, Vd, Sq, causal, softmax_scale, Qc=Qc, Kbar=Kbar)
+        out["O_q"][idx] = O
+        out["lse_q"][idx] = lse
     return out
 
 
