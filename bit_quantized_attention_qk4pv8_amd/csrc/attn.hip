@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
     float d32 = 0.0f;
     if (COMP) {
       if (t == t0 || (t & 31) == 0)
-        compute_delta<D>(dl, a.kbar + (size_t)bg * ntk_max * D, ntk, t & ~31,
+        compute_delta<D>(dl, a.kbar + (size_t)bg * ntk_max * D, t1, t & ~31,
                          a.qbf + ((size_t)b * a.Hq + gk * a.G + 32 * rc) * D, D, a.G - 32 * rc);
       d32 = a.c2 * dl[(t & 31) * 32 + n];
     }
@@ -75,8 +75,16 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
     v16f s[4];
     POp<PV> pb[2];
     int pscale[2];
-    qk_tile<D, PV>(st, lo, buf, s);
-    softmax_tile<D, COMP, PV>(st, s, t, kTile * t + kTile > L, L - 1, d32, pb, pscale);
+    // the compensation offset starts the S accumulator, as in the prefill
+    // (NVFP4 Q/K keeps the add per score)
+    constexpr bool SEED = COMP && PV != QK_NVFP4;
+    v16f init = v16f{};
+    if (SEED) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) init[rr] = d32;
+    }
+    qk_tile<D, PV>(st, lo, buf, s, init);
+    softmax_tile<D, COMP && !SEED, PV>(st, s, t, kTile * t + kTile > L, L - 1, d32, pb, pscale);
     pv_tile<D, PV>(st, lo, buf + TL::V_OFF, pb, pscale);
     wait_vmem_all();
     if (t + 1 < t1) ld.fixup(t + 1, bufs + ((t + 1) & 1) * TL::STRIDE);

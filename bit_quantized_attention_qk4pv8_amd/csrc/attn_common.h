@@ -580,9 +580,13 @@ __device__ __forceinline__ bf16x8 nvfp4_decode8(uint32_t w, float s, float g) {
                 (__bf16)(p2[0] * s), (__bf16)(p2[1] * s), (__bf16)(p3[0] * s), (__bf16)(p3[1] * s)};
 }
 
+// init: the accumulator's start value (zero, or the compensation offset of
+// this lane's row, which then enters the exponent argument through the MFMA's
+// accumulate instead of one add per score).
 template <int D, int PV = PV_FP8>
-__device__ __forceinline__ void qk_blk(const RowState<D>& st, const KBlk<D>& k, v16f& sc_) {
-  sc_ = v16f{};
+__device__ __forceinline__ void qk_blk(const RowState<D>& st, const KBlk<D>& k, v16f& sc_,
+                                       const v16f& init = v16f{}) {
+  sc_ = init;
   if constexpr (PV == QK_NVFP4) {
     // lane group g holds chunk kblock(g, kk) (32 channels); bf16 MFMA 4kk + r
     // contracts its channels 8r .. 8r+7 against the same channels of Q
@@ -649,7 +653,7 @@ struct NoHook {
 template <int D, int PV, class Hook = NoHook>
 __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV>& lo, const uint8_t* vreg,
                                            const POp<PV> (&pb)[2], const int (&pscale)[2], const uint8_t* kreg,
-                                           v16f (&s)[4], const Hook& hook = Hook()) {
+                                           v16f (&s)[4], const v16f& init, const Hook& hook = Hook()) {
   constexpr int NQ = 2 * (D / 32);  // P V products (excluding the denominator)
   constexpr int R = 3;              // V operands in flight
   POp<PV> va[R];
@@ -672,7 +676,7 @@ __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     __builtin_amdgcn_sched_barrier(0);
-    qk_blk<D, PV>(st, kb[c & 1], s[c]);
+    qk_blk<D, PV>(st, kb[c & 1], s[c], init);
     if (c + 2 < 4) load_k_blk<D, PV>(kreg, lo, c + 2, kb[c & 1]);
     hook(NQ + c);
   }
@@ -703,14 +707,14 @@ __device__ __forceinline__ void pv_tile(RowState<D>& st, const LaneOffs<D, PV>& 
 // S = K Q^T of one tile alone, two K blocks in flight.
 template <int D, int PV>
 __device__ __forceinline__ void qk_tile(const RowState<D>& st, const LaneOffs<D, PV>& lo, const uint8_t* kreg,
-                                        v16f (&s)[4]) {
+                                        v16f (&s)[4], const v16f& init = v16f{}) {
   KBlk<D> kb[2];
   load_k_blk<D, PV>(kreg, lo, 0, kb[0]);
   load_k_blk<D, PV>(kreg, lo, 1, kb[1]);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     __builtin_amdgcn_sched_barrier(0);
-    qk_blk<D, PV>(st, kb[c & 1], s[c]);
+    qk_blk<D, PV>(st, kb[c & 1], s[c], init);
     if (c + 2 < 4) load_k_blk<D, PV>(kreg, lo, c + 2, kb[c & 1]);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -740,39 +744,57 @@ __device__ __forceinline__ void store_row(const RowState<D>& st, float* orow, fl
 // FP64 MFMA (v_mfma_f64_16x16x4f64) yields the exactly rounded binary32 value:
 // the per-(row, tile) exponent offset, which decides P codes, is then the same
 // number the binary64 definition gives.  Four 16x16 blocks (2 tile halves x 2
-// row halves); the contraction index of step s, lane group g is channel
-// 32 g + s (any pairing works as long as A and B agree).
+// row halves), each in D/32 steps of 8 channels per lane; the contraction
+// index of step s, element e, lane group g is channel D/4 g + 8 s + e (any
+// pairing works as long as A and B agree).  The operands of a step are loaded
+// one step ahead, across block boundaries, so the FP64 MFMAs do not wait on
+// global-memory latency.  Tiles from tlim on are not needed: their K-bar rows
+// read as zeros, and the blocks of a tile half that starts there are skipped.
 template <int D>
-__device__ __forceinline__ void compute_delta(float* dl, const uint16_t* kbar_bg, int ntk, int tau0,
+__device__ __forceinline__ void compute_delta(float* dl, const uint16_t* kbar_bg, int tlim, int tau0,
                                               const uint16_t* qbase, int q_stride, int nrows_valid) {
   typedef double v4d __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  constexpr int CPG = D / 4;  // channels per lane group
-  // one 16 x 16 block (tile half tb, row half rb) at a time: few live registers
-#pragma unroll 1
-  for (int blk = 0; blk < 4; ++blk) {
-    const int tb = blk >> 1, rb = blk & 1;
-    const int tau = tau0 + 16 * tb + r16, row = 16 * rb + r16;
-    v4d acc = v4d{0.0, 0.0, 0.0, 0.0};
+  constexpr int CPG = D / 4;          // channels per lane group
+  constexpr int NS = CPG / 8;         // steps per block
+  constexpr int NSTEP = 4 * NS;       // steps of the call
+  constexpr int PF = 1;               // steps whose operands are in flight
+  const int nblk = (tau0 + 16 < tlim) ? 4 : 2;  // wave-uniform
+  uint4 ka[PF], qa[PF];
+  auto load = [&](int i, uint4& k, uint4& q) {
+    const int blk = i / NS, c0 = CPG * g + 8 * (i % NS);
+    const int tau = tau0 + 16 * (blk >> 1) + r16, row = 16 * (blk & 1) + r16;
+    k = make_uint4(0u, 0u, 0u, 0u);
+    q = make_uint4(0u, 0u, 0u, 0u);
+    if (blk < nblk && tau < tlim) k = *reinterpret_cast<const uint4*>(kbar_bg + (size_t)tau * D + c0);
+    if (blk < nblk && row < nrows_valid) q = *reinterpret_cast<const uint4*>(qbase + (size_t)row * q_stride + c0);
+  };
+  auto widen = [](const uint4& w, int e) {
+    const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+    return (double)bf16_bits_to_float((x >> ((e & 1) ? 16 : 0)) & 0xFFFFu);
+  };
 #pragma unroll
-    for (int s8 = 0; s8 < CPG; s8 += 8) {
-      const int c0 = CPG * g + s8;
-      uint4 ka = {0u, 0u, 0u, 0u}, qa = {0u, 0u, 0u, 0u};
-      if (tau < ntk) ka = *reinterpret_cast<const uint4*>(kbar_bg + (size_t)tau * D + c0);
-      if (row < nrows_valid) qa = *reinterpret_cast<const uint4*>(qbase + (size_t)row * q_stride + c0);
-      const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w}, qaw[4] = {qa.x, qa.y, qa.z, qa.w};
+  for (int i = 0; i < PF; ++i) load(i, ka[i], qa[i]);
+  // two independent accumulation chains (even and odd elements), so one
+  // MFMA need not wait for the previous one's result; their sum is exact too
+  v4d acc[2] = {v4d{0.0, 0.0, 0.0, 0.0}, v4d{0.0, 0.0, 0.0, 0.0}};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) ? 16 : 0;
-        const double A = (double)bf16_bits_to_float((kaw[e >> 1] >> sh) & 0xFFFFu);
-        const double B = (double)bf16_bits_to_float((qaw[e >> 1] >> sh) & 0xFFFFu);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(A, B, acc, 0, 0, 0);
-      }
+  for (int i = 0; i < NSTEP; ++i) {
+    const int blk = i / NS;
+    if (blk >= nblk) break;
+    const uint4 k = ka[i % PF], q = qa[i % PF];
+    if (i + PF < NSTEP) load(i + PF, ka[i % PF], qa[i % PF]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc[e & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(widen(k, e), widen(q, e), acc[e & 1], 0, 0, 0);
+    if (i % NS == NS - 1) {
+      // FP64 16x16 result layout: register r of lane l holds entry (i, j) = (l / 16 + 4 r, l % 16):
+      // tile 16 tb + lane / 16 + 4 r, query row 16 rb + lane % 16
+      const int tb = blk >> 1, rb = blk & 1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dl[(16 * tb + g + 4 * r) * 32 + 16 * rb + r16] = (float)(acc[0][r] + acc[1][r]);
+      acc[0] = acc[1] = v4d{0.0, 0.0, 0.0, 0.0};
     }
-    // FP64 16x16 result layout: register r of lane l holds entry (i, j) = (l / 16 + 4 r, l % 16):
-    // tile 16 tb + lane / 16 + 4 r, query row 16 rb + lane % 16
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dl[(16 * tb + g + 4 * r) * 32 + 16 * rb + r16] = (float)acc[r];
   }
 }
 

@@ -197,17 +197,30 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
     const bool do_pv = t >= 1 && t - 1 < Tw, do_qk = t < Tw;
     v16f s[4];  // S of tile t: written here, consumed by this iteration's softmax
     if (COMP && do_qk && (t & 31) == 0)
-      compute_delta<D>(dl, a.kbar + (size_t)grp * ntk * D, ntk, t, a.qbf + (((size_t)b * a.Hq + h) * Sq + i0) * D, D,
+      compute_delta<D>(dl, a.kbar + (size_t)grp * ntk * D, Tw, t, a.qbf + (((size_t)b * a.Hq + h) * Sq + i0) * D, D,
                        Sq - i0);
+    // The compensation offset d = fl32(c2 fl32(delta)) of this lane's row and
+    // tile starts the S accumulator, so the exponent argument
+    // y = fl32(fl32(d + S'_0) + S'_1) (S'_k: the exact partial product of
+    // MFMA k) needs no add per score.  (NVFP4 Q/K, a contrast format on the
+    // bf16 MFMA, keeps the add: its register budget has no room for the
+    // start value.)
+    constexpr bool SEED = COMP && PV != QK_NVFP4;
+    v16f init = v16f{};
+    if (SEED) {
+      const float d32 = a.c2 * dl[(t & 31) * 32 + n];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) init[rr] = d32;
+    }
     __builtin_amdgcn_s_setprio(2);
     // (a wave's last P V also computes a product of whatever K buffer kb_cur
     // holds; that S is never used: one code path keeps the register budget)
     if (do_pv) {
-      pv_then_qk<D, PV>(st, lo, vbuf + vb_prev * TL::VREG, pb, pscale, kbuf + kb_cur * TL::KREG, s, dma);
+      pv_then_qk<D, PV>(st, lo, vbuf + vb_prev * TL::VREG, pb, pscale, kbuf + kb_cur * TL::KREG, s, init, dma);
     } else {
 #pragma unroll
       for (int k = 0; k <= SLOTS; ++k) dma(k);
-      if (do_qk) qk_tile<D, PV>(st, lo, kbuf + kb_cur * TL::KREG, s);
+      if (do_qk) qk_tile<D, PV>(st, lo, kbuf + kb_cur * TL::KREG, s, init);
     }
     __builtin_amdgcn_s_setprio(0);
     // ---- end of this wave's window: its loads of K(t+1) and V(t) (issued
@@ -224,9 +237,9 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
     if (half == 1) end_window();
     // ---- softmax of tile t
     if (t < Tw) {
-      const float d32 = COMP ? a.c2 * dl[(t & 31) * 32 + n] : 0.0f;
+      const float d32 = (COMP && !SEED) ? a.c2 * dl[(t & 31) * 32 + n] : 0.0f;
       const bool need_mask = (kTile * t + kTile - 1 > jmin_w) || (kTile * t + kTile > L);
-      softmax_tile<D, COMP, PV>(st, s, t, need_mask, jlim, d32, pb, pscale);
+      softmax_tile<D, COMP && !SEED, PV>(st, s, t, need_mask, jlim, d32, pb, pscale);
     }
     if (half == 0) end_window();
     kb_cur = kb_cur + 1 == NB ? 0 : kb_cur + 1;
