@@ -148,8 +148,12 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   uint8_t* trash = smem + NB * (TL::KREG + TL::VREG);     // 1 KB sink of unused DMA slots
   float* dl = reinterpret_cast<float*>(trash + 1024) + wave * 32 * 32;
 
-  // All buffers start zeroed: bytes a ragged tile does not cover then hold
-  // zeros or codes of an earlier tile, never uninitialised (possibly NaN) codes.
+  // Every byte a tile step reads is written by that tile's DMA first, and the
+  // DMA writes zeros for the lanes its range check cuts off, so a ragged tile
+  // reads zeros without this (the decode relies on exactly that).  The buffers
+  // are zeroed once anyway, at about 0.3% of the kernel's time, so that a
+  // byte read outside the DMA's coverage could only ever be zero, never a
+  // leftover NaN code.
   for (int o = threadIdx.x * 16; o < NB * (TL::KREG + TL::VREG); o += blockDim.x * 16)
     *reinterpret_cast<uint4*>(smem + o) = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
