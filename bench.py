@@ -580,6 +580,7 @@ def main():
             log("config", name)
             wc = WORKLOADS[name]
             rec, inp = run_prefill(wc, args, dev, stream, step_mode=False)
+            rec["roofline"]["traffic"] = traffic_from_profile("prefill_%s_traffic.json" % name, src)
             if wc.smooth:
                 log("config", name, "compensation off")
                 off, _ = run_prefill(wc, args, dev, stream, smooth=False, inp=inp, step_mode=False)
