@@ -14,6 +14,8 @@
 //  - probe_s_tile: one 128-key tile of S' = Q'4 K4^T for 32 query rows, through
 //    the kernels' own tile DMA, operand reads and block-scaled FP4 MFMAs
 //    (attn_common.h), written out as binary32 scores.
+//  - probe_s_tile_seeded: the same tile with the S accumulator started at a
+//    per-row offset d[row], as the compensated kernels start it.
 //  - probe_lds_fill: fills the LDS of every compute unit with a byte pattern
 //    (a regression check that no kernel reads LDS bytes it did not write).
 //
@@ -59,9 +61,10 @@ __global__ void k_cvt(int kind, const float* __restrict__ x, long n, float scale
 // One wave: query rows 0..31 (codes q4 [32][D/2], scales [32][D/32]) against
 // keys [128 t, 128 t + 128) of k4 [L][D/2], k4s [L][D/32].  S[row][key] for
 // the keys present (a ragged last tile writes only its L - 128 t keys).
+// d: null, or 32 per-row start values of the accumulator.
 template <int D>
 __global__ void __launch_bounds__(64) k_s_tile(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4,
-                                               const uint8_t* k4s, int L, int t, float* S) {
+                                               const uint8_t* k4s, const float* d, int L, int t, float* S) {
   using TL = TileLayout<D, PV_FP8>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
@@ -76,7 +79,13 @@ __global__ void __launch_bounds__(64) k_s_tile(const uint8_t* q4, const uint8_t*
   LaneOffs<D, PV_FP8> lo;
   lo.init();
   v16f s[4];
-  qk_tile<D, PV_FP8>(st, lo, smem, s);
+  v16f init = v16f{};
+  if (d) {
+    const float dn = d[n];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) init[rr] = dn;
+  }
+  qk_tile<D, PV_FP8>(st, lo, smem, s, init);
   const int nk = min(kTile, L - kTile * t);
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -105,19 +114,24 @@ int probe_cvt(int kind, const float* x, long n, float scale, uint8_t* out) {
   return (int)hipGetLastError();
 }
 
-int probe_s_tile(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s, int D, int L, int t,
-                 float* S) {
+int probe_s_tile_seeded(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s, const float* d,
+                        int D, int L, int t, float* S) {
   if (L <= 0 || t < 0 || kTile * t >= L) return (int)hipErrorInvalidValue;
   if (D == 64) {
     constexpr size_t lds = TileLayout<64, PV_FP8>::KREG;
-    hipLaunchKernelGGL(k_s_tile<64>, dim3(1), dim3(64), lds, 0, q4, q4s, k4, k4s, L, t, S);
+    hipLaunchKernelGGL(k_s_tile<64>, dim3(1), dim3(64), lds, 0, q4, q4s, k4, k4s, d, L, t, S);
   } else if (D == 128) {
     constexpr size_t lds = TileLayout<128, PV_FP8>::KREG;
-    hipLaunchKernelGGL(k_s_tile<128>, dim3(1), dim3(64), lds, 0, q4, q4s, k4, k4s, L, t, S);
+    hipLaunchKernelGGL(k_s_tile<128>, dim3(1), dim3(64), lds, 0, q4, q4s, k4, k4s, d, L, t, S);
   } else {
     return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
+}
+
+int probe_s_tile(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const uint8_t* k4s, int D, int L, int t,
+                 float* S) {
+  return probe_s_tile_seeded(q4, q4s, k4, k4s, nullptr, D, L, t, S);
 }
 
 // Every workgroup takes `bytes` of LDS (at most 160 KB) and writes the pattern into all of it.
