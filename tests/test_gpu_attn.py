@@ -109,6 +109,17 @@ def test_prefill_compensation_beyond_32_tiles():
     _check_prefill(q, k, v, False, 1 / math.sqrt(128), True, _all_rows(1, 2, 64), "comp-5000keys")
 
 
+@pytest.mark.parametrize("D,S,fused", [(64, 4500, False), (128, 4200, True)])
+def test_prefill_compensation_causal_many_tiles(D, S, fused):
+    """Causal rows whose delta chunks (32 tiles) end inside the wave's range,
+    a chunk boundary at key 4096, a ragged last tile, and tile halves of a
+    chunk that lie past a wave's last tile (skipped by the delta product)."""
+    q, k, v = _rand_inputs(1, 4, 2, S, S, D, seed=D + S, k_offset=3.0, q_scale=2.0)
+    must = (0, 31, 32, 2047, 2048, 2049, 4063, 4064, 4095, 4096, 4097, 4127, 4128)
+    rows = sample_rows(1, 4, S, 360, seed=S, must=must)
+    _check_prefill(q, k, v, True, 1.0 / math.sqrt(D), True, rows, "comp-causal-D%d-S%d" % (D, S), fused=fused)
+
+
 FUSED_CASES = [
     (1, 4, 2, 300, 300, 128, True, False, 0.0, "fused-causal-ragged-D128"),
     (1, 5, 1, 70, 333, 64, True, False, 0.0, "fused-bottom-right-G5-D64"),
