@@ -6,9 +6,9 @@
 //   softmax       mask, running max on the integer grid, P = E4M3(256 * 2^(.))
 //                 packed directly as the B operand of the P V product
 //                                                                [softmax_tile]
-//   P V           O^T += V^T P^T and the denominator 1 . P^T on the FP8 MFMA,
-//                 with the rescale 2^(m - m_ref) riding on P's E8M0 scale
-//                                                                [pv_tile]
+//   P V           O^T += V^T P^T on the FP8 MFMA, with the rescale
+//                 2^(m - m_ref) riding on P's E8M0 scale, and the tile's row
+//                 sums of P on one 16x16x128 MFMA per 64 keys   [pv_tile]
 // pv_then_qk runs the P V of one tile and the S^T of the next back to back.
 // Every step is templated on the kernel format: the method (above) or one of
 // the contrast formats described at pv_of below.
@@ -324,11 +324,13 @@ struct RowState {
   v4i qa[D / 64];  // Q fragments (B operand of S^T = K Q^T), channel blocks kblock(g, k)
   int qs;          // their E8M0 scale bytes: byte k feeds MFMA k
   v16f o[D / 32];  // O^T accumulators: o[cb][rr] = channel 32cb + (rr/4)*8 + 4g + rr%4
-  v16f lv;         // denominator 1 . P^T (every element equals the row sum), in the m_ref frame
+  float lsum;      // E4M3 P: the denominator, sum of 2^(m_t - m_ref) times tile t's row sum of P codes
+  v4i sel;         // E4M3 P: the E2M1 selector operand of the row sums (see tile_rowsum)
+  v16f lv;         // block-scaled P: denominator 1 . P^T (every element equals the row sum)
   float m;         // running max in log2 units, on the integer grid (-inf before any key)
-  float m_ref;     // frame of o and lv: both hold sum 2^(m_t - m_ref) P_t (V_t | 1)
-  v8i ones;        // 1.0 in every element (E4M3 0x38, or E2M1 0x2 in the first four dwords): the A
-                   // operand of the denominator product
+  float m_ref;     // frame of o and the denominator: sum 2^(m_t - m_ref) P_t (V_t | 1)
+  v8i ones;        // block-scaled P: 1.0 in every element (E4M3 0x38, or E2M1 0x2 in the first four
+                   // dwords), the A operand of the denominator product
   bf16x8 qn[D / 16];  // QK_NVFP4: Q decoded to bf16, 8 channels per bf16 MFMA (see qk_blk)
   float gk;           // QK_NVFP4: K's tensor scale
 };
@@ -447,8 +449,12 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(st.o[cb][rr]) : "v"(f));
+    if constexpr (P == PV_FP8) {
+      st.lsum *= f;
+    } else {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(st.lv[rr]) : "v"(f));
+      for (int rr = 0; rr < 16; ++rr) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(st.lv[rr]) : "v"(f));
+    }
     if (mn - st.m_ref > 64.0f) st.m_ref = mn;
   }
   // ---- P8 = E4M3(256 * 2^(y - e)), packed as the B operand of O^T += V^T P^T,
@@ -636,9 +642,34 @@ __device__ __forceinline__ POp<PV> ones_op(const v8i& ones) {
     return ones;
 }
 
+// Row sums of the E4M3 P codes of one 64-key half, accumulated into ts, on
+// one 16x16x128 MFMA at unit scales.  Read as the B operand of that product,
+// the 32x32x64 P operand pb (lane l: query l % 32) gives output column c the
+// codes of query c from lane groups 0 and 2 and of query c + 16 from groups 1
+// and 3; with the E4M3 index layout (see mfma_fp4_fp8_16x16x128) these are
+// exactly the contraction indices with bit 4 clear and set.  The selector
+// operand st.sel holds E2M1 ones in nibbles 0..15 (indices with bit 4 clear)
+// for rows r with bit 2 clear and in nibbles 16..31 for the others, so output
+// (r, c) sums query c + 16 ((r >> 2) & 1); the rows lane l holds,
+// 4 (l / 16) .. 4 (l / 16) + 3, then make all four of its elements the sum of
+// its own query l % 32.  P's row scale cannot ride on this product (a 32-index
+// scale block mixes two queries), so the sum is taken in P's own frame and
+// folded into st.lsum with the factor 2^(m - m_ref) by one FMA.  The result is
+// bit-identical to the 32x32x64 product against E4M3 ones at unit scale
+// (checked on MI355X), at half the matrix time and a quarter of the registers.
+__device__ __forceinline__ v4f tile_rowsum(const v4i& sel, const v8i& pb, const v4f& ts) {
+  return mfma_fp4_fp8_16x16x128(sel, pb, ts);
+}
+// lsum += 2^(m - m_ref) * (tile row sum), the factor read from P's scale code.
+template <int D>
+__device__ __forceinline__ void fold_rowsum(RowState<D>& st, const v4f& ts, int pscale) {
+  st.lsum = __builtin_fmaf(ts[0], __builtin_ldexpf(1.0f, pscale - kScaleOne), st.lsum);
+}
+
 // O^T += 2^(m - m_ref) V^T P^T of one tile (FP8 x FP8; V's E8M0 scale per 32
-// tokens x channel, P's per row) and the denominator, the same product
-// against ones, followed by S = K Q^T of the next tile.  Software-pipelined
+// tokens x channel, P's per row) and the denominator (tile_rowsum for E4M3 P;
+// for block-scaled P the same product against ones), followed by S = K Q^T of
+// the next tile.  Software-pipelined
 // over a small ring of operand registers: V operands are read three products
 // ahead and the first two K blocks during the last P V products, so the MFMAs
 // issue back to back while LDS reads stay in flight.  The scheduler fences
@@ -656,9 +687,11 @@ __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV
                                            v16f (&s)[4], const v16f& init, const Hook& hook = Hook()) {
   constexpr int NQ = 2 * (D / 32);  // P V products (excluding the denominator)
   constexpr int R = 3;              // V operands in flight
+  constexpr bool TS = pv_of(PV) == PV_FP8;
   POp<PV> va[R];
   int vs[R];
   KBlk<D> kb[2];
+  v4f ts = v4f{};
 #pragma unroll
   for (int q = 0; q < R; ++q) load_v_op<D, PV>(vreg, lo, q, va[q], vs[q]);
 #pragma unroll
@@ -666,7 +699,12 @@ __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV
     __builtin_amdgcn_sched_barrier(0);
     const int h = q / (D / 32), cb = q % (D / 32);
     st.o[cb] = mfma_pv<PV>(va[q % R], pb[h], st.o[cb], vs[q % R], pscale[h]);
-    if (cb == D / 32 - 1) st.lv = mfma_pv<PV>(ones_op<PV>(st.ones), pb[h], st.lv, kScaleOne, pscale[h]);
+    if (cb == D / 32 - 1) {
+      if constexpr (TS)
+        ts = tile_rowsum(st.sel, pb[h], ts);
+      else
+        st.lv = mfma_pv<PV>(ones_op<PV>(st.ones), pb[h], st.lv, kScaleOne, pscale[h]);
+    }
     if (q + R < NQ)
       load_v_op<D, PV>(vreg, lo, q + R, va[q % R], vs[q % R]);
     else if (q + R - NQ < 2)
@@ -681,6 +719,8 @@ __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV
     hook(NQ + c);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // (the row sums finished during the S products)
+  if constexpr (TS) fold_rowsum(st, ts, pscale[0]);
 }
 
 // P V of one tile alone, pipelined like pv_then_qk.
@@ -689,8 +729,10 @@ __device__ __forceinline__ void pv_tile(RowState<D>& st, const LaneOffs<D, PV>& 
                                         const POp<PV> (&pb)[2], const int (&pscale)[2]) {
   constexpr int NQ = 2 * (D / 32);
   constexpr int R = 3;
+  constexpr bool TS = pv_of(PV) == PV_FP8;
   POp<PV> va[R];
   int vs[R];
+  v4f ts = v4f{};
 #pragma unroll
   for (int q = 0; q < R; ++q) load_v_op<D, PV>(vreg, lo, q, va[q], vs[q]);
 #pragma unroll
@@ -698,10 +740,16 @@ __device__ __forceinline__ void pv_tile(RowState<D>& st, const LaneOffs<D, PV>& 
     __builtin_amdgcn_sched_barrier(0);
     const int h = q / (D / 32), cb = q % (D / 32);
     st.o[cb] = mfma_pv<PV>(va[q % R], pb[h], st.o[cb], vs[q % R], pscale[h]);
-    if (cb == D / 32 - 1) st.lv = mfma_pv<PV>(ones_op<PV>(st.ones), pb[h], st.lv, kScaleOne, pscale[h]);
+    if (cb == D / 32 - 1) {
+      if constexpr (TS)
+        ts = tile_rowsum(st.sel, pb[h], ts);
+      else
+        st.lv = mfma_pv<PV>(ones_op<PV>(st.ones), pb[h], st.lv, kScaleOne, pscale[h]);
+    }
     if (q + R < NQ) load_v_op<D, PV>(vreg, lo, q + R, va[q % R], vs[q % R]);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (TS) fold_rowsum(st, ts, pscale[0]);
 }
 
 // S = K Q^T of one tile alone, two K blocks in flight.
@@ -726,7 +774,7 @@ __device__ __forceinline__ void qk_tile(const RowState<D>& st, const LaneOffs<D,
 template <int D, int PV = PV_FP8>
 __device__ __forceinline__ void store_row(const RowState<D>& st, float* orow, float* lse_row) {
   const int g = (threadIdx.x & 63) >> 5;
-  const float l = st.lv[0];
+  const float l = pv_of(PV) == PV_FP8 ? st.lsum : st.lv[0];
   const bool empty = (st.m == -__builtin_inff());
   const float inv = empty ? 0.0f : 1.0f / l;
 #pragma unroll
@@ -844,12 +892,22 @@ __device__ __forceinline__ void load_q(RowState<D>& st, const uint8_t* q4row, co
   }
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) st.o[cb] = v16f{};
-  st.lv = v16f{};
   st.m = -__builtin_inff();
   st.m_ref = -__builtin_inff();
-  constexpr int one = PV == PV_FP4 ? 0x22222222 : 0x38383838;  // E2M1 / E4M3 1.0 in every element
-  st.ones = v8i{one, one, one, one, one, one, one, one};
-  asm volatile("" : "+v"(st.ones));  // resident in VGPRs for the whole loop (no per-tile rebuild)
+  if constexpr (pv_of(PV) == PV_FP8) {
+    st.lsum = 0.0f;
+    // tile_rowsum's selector: E2M1 1.0 (0x2) in nibbles 0..15 for rows r = lane % 16
+    // with bit 2 clear, in nibbles 16..31 for the others
+    constexpr int e = 0x22222222;
+    const bool hi = (threadIdx.x >> 2) & 1;
+    st.sel = v4i{hi ? 0 : e, hi ? 0 : e, hi ? e : 0, hi ? e : 0};
+    asm volatile("" : "+v"(st.sel));  // resident in VGPRs for the whole loop (no per-tile rebuild)
+  } else {
+    st.lv = v16f{};
+    constexpr int one = PV == PV_FP4 ? 0x22222222 : 0x38383838;  // E2M1 / E4M3 1.0 in every element
+    st.ones = v8i{one, one, one, one, one, one, one, one};
+    asm volatile("" : "+v"(st.ones));  // resident in VGPRs for the whole loop (no per-tile rebuild)
+  }
 }
 
 }  // namespace qfa

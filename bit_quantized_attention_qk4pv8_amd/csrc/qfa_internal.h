@@ -160,6 +160,16 @@ __device__ __forceinline__ v16f mfma_fp4_32x32x64_sel(v4i a, v4i b, v16f c, int 
 __device__ __forceinline__ v16f mfma_fp8_32x32x64(v8i a, v8i b, v16f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
+// 16x16x128, E2M1 A (four VGPRs) x E4M3 B, unit scales.  Lane l supplies row
+// (or column) l % 16.  For E4M3 operands lane group g = l / 16 holds
+// contraction indices 16g + (0..15) in bytes 0..15 and 64 + 16g + (0..15) in
+// bytes 16..31, and the scale of each 32-index block is taken from one lane
+// group, so a block mixes bytes of two lane groups; E2M1 operands hold
+// indices 32g + (0..31) in nibble order (both measured on MI355X).
+__device__ __forceinline__ v4f mfma_fp4_fp8_16x16x128(v4i a, v8i b, v4f c) {
+  v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, 4, 0, 0, kScaleOne, 0, kScaleOne);
+}
 
 // ---------------------------------------------------------------- launchers (host side)
 hipError_t launch_quant_qk4(const uint16_t* x, int B, int H, int S, int D, int smooth, float prescale,

@@ -16,6 +16,9 @@
 //    (attn_common.h), written out as binary32 scores.
 //  - probe_s_tile_seeded: the same tile with the S accumulator started at a
 //    per-row offset d[row], as the compensated kernels start it.
+//  - probe_tile_rowsum: the E4M3-P denominator of two tiles (tile_rowsum on
+//    each 64-key half, then fold_rowsum with each tile's P scale code), for
+//    P operands given in the 32x32x64 B layout of the P V product.
 //  - probe_lds_fill: fills the LDS of every compute unit with a byte pattern
 //    (a regression check that no kernel reads LDS bytes it did not write).
 //
@@ -104,6 +107,27 @@ __global__ void __launch_bounds__(256) k_lds_fill(uint32_t pattern, int words) {
 
 }  // namespace
 
+// pb: per lane 32 dwords (tile t, half h at dwords 16t + 8h .. +7); ps: per
+// lane the P scale codes of the two tiles.  ts_out[(t * 64 + lane) * 4 + v]:
+// element v of tile t's row sums; lsum_out[lane]: the denominator after both.
+__global__ void __launch_bounds__(64) k_tile_rowsum(const int* pb, const int* ps, float* ts_out, float* lsum_out) {
+  const int lane = threadIdx.x;
+  RowState<64> st;
+  load_q<64, PV_FP8>(st, nullptr, nullptr, nullptr, 1.0f, false);
+  for (int t = 0; t < 2; ++t) {
+    v8i p0, p1;
+    for (int r = 0; r < 8; ++r) {
+      p0[r] = pb[lane * 32 + 16 * t + r];
+      p1[r] = pb[lane * 32 + 16 * t + 8 + r];
+    }
+    v4f ts = tile_rowsum(st.sel, p0, v4f{});
+    ts = tile_rowsum(st.sel, p1, ts);
+    fold_rowsum(st, ts, ps[lane * 2 + t]);
+    for (int v = 0; v < 4; ++v) ts_out[(t * 64 + lane) * 4 + v] = ts[v];
+  }
+  lsum_out[lane] = st.lsum;
+}
+
 extern "C" {
 
 int probe_cvt(int kind, const float* x, long n, float scale, uint8_t* out) {
@@ -135,6 +159,11 @@ int probe_s_tile(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const
 }
 
 // Every workgroup takes `bytes` of LDS (at most 160 KB) and writes the pattern into all of it.
+int probe_tile_rowsum(const int* pb, const int* ps, float* ts_out, float* lsum_out) {
+  hipLaunchKernelGGL(k_tile_rowsum, dim3(1), dim3(64), 0, 0, pb, ps, ts_out, lsum_out);
+  return (int)hipGetLastError();
+}
+
 int probe_lds_fill(uint32_t pattern, int nwg, int bytes) {
   if (nwg <= 0 || bytes <= 0 || bytes > 160 * 1024 || (bytes & 3)) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(k_lds_fill, dim3(nwg), dim3(256), (size_t)bytes, 0, pattern, bytes / 4);

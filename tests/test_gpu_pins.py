@@ -12,6 +12,11 @@ section 5.2; the E2M1 values of the FP4 tutorial, section
 driven with the power-of-two scale operands the kernels pass (2^(m - 8) for
 E4M3 P with m in [-100, 100]; 2^(e - 2) for E2M1 P), so x / scale is exact.
 
+Row sums.  The E4M3-P denominator (one 16x16x128 MFMA per 64 keys against an
+E2M1 selector, then one FMA per tile) must give every lane the sum of its own
+query's P codes; checked on edge patterns that must match to the bit and on
+random codes against exact sums.
+
 S tile.  One 128-key tile of S' = Q'4 K4^T from the block-scaled FP4 MFMA,
 through the kernels' own tile DMA and operand layout, is compared bit for bit
 with the oracle's exact Q' . K (binary64) on workload-shaped inputs: the
@@ -244,6 +249,70 @@ def test_s_tile_seeded_accumulator_error_bound(probe, kind, D, L):
         total += got.size
     say("seeded S %s D%d: error <= %.2f x 2^-24 of the summed magnitudes (bound %d); %d of %d scores differ "
         "from fl32(fl32(S') + d)" % (kind, D, worst, nb, differs, total))
+
+
+def _rowsum_inputs(case, rng):
+    """P codes per (lane, tile, half, byte) in the 32x32x64 B layout of the
+    P V product (lane l holds 32 keys of query l % 32), and per-query scale
+    codes 2^(m - m_ref) (the same for lanes l and l + 32, as the kernels pass)."""
+    codes = np.zeros((64, 2, 2, 32), dtype=np.uint8)
+    query = np.arange(64) % 32
+    if case == "random":
+        codes[:] = rng.integers(0, 0x7F, size=codes.shape)          # every finite E4M3 code >= 0
+        codes[rng.random(codes.shape) < 0.3] = 0
+    elif case == "ones":
+        codes[:] = 0x38
+    elif case == "query_halves":                                      # queries 0..15 only, then 16..31 only
+        codes[query < 16, 0] = 0x38
+        codes[query >= 16, 1] = 0x38
+    elif case == "lane_groups":                                       # only lanes 32..63 (second key half)
+        codes[32:] = 0x38
+    elif case == "extremes":                                          # 448 beside subnormals
+        codes[:] = rng.choice(np.array([0x7E, 0x01, 0x07, 0x08, 0x00], dtype=np.uint8), size=codes.shape)
+    qs = rng.integers(0, 65, size=(32, 2))
+    ps = (127 + qs[query]).astype(np.int32)                         # (64, 2)
+    return codes, ps
+
+
+@pytest.mark.parametrize("case", ["ones", "query_halves", "lane_groups", "random", "extremes"])
+def test_tile_rowsum_sums_each_lanes_own_query(probe, case):
+    """The E4M3-P denominator: per 64-key half one 16x16x128 MFMA (E2M1
+    selector x the P operand, unit scales), then lsum += 2^(m - m_ref) x the
+    tile's row sum.  Every element of lane l must carry the row sum of query
+    l % 32.  Sums of E4M3 1.0 codes are exact, so the selection cases must
+    match to the bit; on random codes the matrix unit's FP8 accumulation is
+    not exact (measured up to 1.0e-4 relative, with 448 beside subnormals),
+    so the bound there is 2^-12,
+    far below the error of a wrong selection (a whole query's sum)."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(len(case))
+    codes, ps = _rowsum_inputs(case, rng)
+    pb = torch.from_numpy(np.ascontiguousarray(codes).view(np.int32).reshape(64, 32)).to(dev)
+    pst = torch.from_numpy(np.ascontiguousarray(ps)).to(dev)
+    ts = torch.full((2, 64, 4), float("nan"), dtype=torch.float32, device=dev)
+    lsum = torch.full((64,), float("nan"), dtype=torch.float32, device=dev)
+    say("tile row sums: %s" % case)
+    rc = probe.probe_tile_rowsum(pb.data_ptr(), pst.data_ptr(), ts.data_ptr(), lsum.data_ptr())
+    assert rc == 0, rc
+    torch.cuda.synchronize()
+    ts, lsum = to_np(ts).astype(np.float64), to_np(lsum).astype(np.float64)
+    val = np.array([oracle.e4m3_value(c) for c in range(256)])
+    per_lane = val[codes].sum(axis=(2, 3))                           # (64, 2): tile sums of a lane's keys
+    exact = np.zeros((32, 2))
+    np.add.at(exact, np.arange(64) % 32, per_lane)
+    want = exact[np.arange(64) % 32]                                 # (64, 2)
+    assert np.array_equal(ts, np.repeat(ts[..., :1], 4, axis=-1)), "a lane's four elements differ"
+    got = ts[..., 0].T                                               # (64, 2)
+    want_l = (want * 2.0 ** (ps - 127)).sum(axis=1)
+    if case in ("ones", "query_halves", "lane_groups"):
+        assert np.array_equal(got, want), (got, want)
+        # two FMAs: the first term is exact, the second rounds the exact sum once
+        assert np.array_equal(lsum, want_l.astype(np.float32).astype(np.float64)), (lsum, want_l)
+    else:
+        rel = np.abs(got - want) / np.maximum(want, 1e-30)
+        rl = np.abs(lsum - want_l) / np.maximum(want_l, 1e-30)
+        say("tile row sums %s: worst relative error %.3g (tile), %.3g (denominator)" % (case, rel.max(), rl.max()))
+        assert rel.max() <= 2.0 ** -12 and rl.max() <= 2.0 ** -12, (rel.max(), rl.max())
 
 
 @pytest.mark.parametrize("D,lens", [(64, [5, 517, 129, 1]), (128, [517, 5, 255, 130])])
