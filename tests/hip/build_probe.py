@@ -20,7 +20,7 @@ FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
-SYMBOLS = ("probe_cvt", "probe_s_tile", "probe_s_tile_seeded", "probe_tile_rowsum", "probe_lds_fill")
+SYMBOLS = ("probe_cvt", "probe_s_tile", "probe_s_tile_seeded", "probe_tile_rowsum", "probe_delta", "probe_lds_fill")
 
 
 def build(verbose: bool = False) -> str:
@@ -52,6 +52,8 @@ def load():
     L.probe_s_tile_seeded.argtypes = [P, P, P, P, P, I, I, I, P]
     L.probe_tile_rowsum.restype = I
     L.probe_tile_rowsum.argtypes = [P, P, P, P]
+    L.probe_delta.restype = I
+    L.probe_delta.argtypes = [P, I, I, P, I, I, I, P]
     L.probe_lds_fill.restype = I
     L.probe_lds_fill.argtypes = [ctypes.c_uint32, I, I]
     return L

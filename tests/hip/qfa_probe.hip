@@ -19,6 +19,9 @@
 //  - probe_tile_rowsum: the E4M3-P denominator of two tiles (tile_rowsum on
 //    each 64-key half, then fold_rowsum with each tile's P scale code), for
 //    P operands given in the 32x32x64 B layout of the P V product.
+//  - probe_delta: the rank-one compensation term of 32 tiles x 32 query rows
+//    (compute_delta: K-bar . Q_bf16 on the FP64 MFMA), written out as the
+//    LDS slab the kernels read, dl[tile][row].
 //  - probe_lds_fill: fills the LDS of every compute unit with a byte pattern
 //    (a regression check that no kernel reads LDS bytes it did not write).
 //
@@ -128,6 +131,17 @@ __global__ void __launch_bounds__(64) k_tile_rowsum(const int* pb, const int* ps
   lsum_out[lane] = st.lsum;
 }
 
+template <int D>
+__global__ void __launch_bounds__(64) k_delta(const uint16_t* kbar, int tlim, int tau0, const uint16_t* q,
+                                               int q_stride, int nrows, float* out) {
+  __shared__ float dl[32 * 32];
+  for (int o = threadIdx.x; o < 32 * 32; o += 64) dl[o] = __builtin_nanf("");
+  __syncthreads();
+  compute_delta<D>(dl, kbar, tlim, tau0, q, q_stride, nrows);
+  __syncthreads();
+  for (int o = threadIdx.x; o < 32 * 32; o += 64) out[o] = dl[o];
+}
+
 extern "C" {
 
 int probe_cvt(int kind, const float* x, long n, float scale, uint8_t* out) {
@@ -161,6 +175,20 @@ int probe_s_tile(const uint8_t* q4, const uint8_t* q4s, const uint8_t* k4, const
 // Every workgroup takes `bytes` of LDS (at most 160 KB) and writes the pattern into all of it.
 int probe_tile_rowsum(const int* pb, const int* ps, float* ts_out, float* lsum_out) {
   hipLaunchKernelGGL(k_tile_rowsum, dim3(1), dim3(64), 0, 0, pb, ps, ts_out, lsum_out);
+  return (int)hipGetLastError();
+}
+
+// kbar: the K-bar rows of one slice (tile-major, D bf16 each; at least one
+// row, and every row below tlim); q: the first of 32 query rows, q_stride
+// elements apart (rows below nrows are read); out: 32 x 32 floats.
+int probe_delta(const uint16_t* kbar, int tlim, int tau0, const uint16_t* q, int q_stride, int nrows, int D,
+                float* out) {
+  if (D == 64)
+    hipLaunchKernelGGL(k_delta<64>, dim3(1), dim3(64), 0, 0, kbar, tlim, tau0, q, q_stride, nrows, out);
+  else if (D == 128)
+    hipLaunchKernelGGL(k_delta<128>, dim3(1), dim3(64), 0, 0, kbar, tlim, tau0, q, q_stride, nrows, out);
+  else
+    return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
 

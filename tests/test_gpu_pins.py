@@ -17,6 +17,10 @@ E2M1 selector, then one FMA per tile) must give every lane the sum of its own
 query's P codes; checked on edge patterns that must match to the bit and on
 random codes against exact sums.
 
+Delta.  The rank-one compensation term (K-bar . q_bf16 for 32 tiles x 32
+rows) on the FP64 MFMA must equal fl32 of the exact sum bit for bit, with
+zeros past the valid tiles and rows.
+
 S tile.  One 128-key tile of S' = Q'4 K4^T from the block-scaled FP4 MFMA,
 through the kernels' own tile DMA and operand layout, is compared bit for bit
 with the oracle's exact Q' . K (binary64) on workload-shaped inputs: the
@@ -313,6 +317,45 @@ def test_tile_rowsum_sums_each_lanes_own_query(probe, case):
         rl = np.abs(lsum - want_l) / np.maximum(want_l, 1e-30)
         say("tile row sums %s: worst relative error %.3g (tile), %.3g (denominator)" % (case, rel.max(), rl.max()))
         assert rel.max() <= 2.0 ** -12 and rl.max() <= 2.0 ** -12, (rel.max(), rl.max())
+
+
+@pytest.mark.parametrize("kind,D,ntiles,tau0,tlim,nrows", [
+    ("offset", 128, 32, 0, 32, 32), ("outlier", 128, 32, 0, 32, 32), ("offset", 64, 32, 0, 32, 32),
+    ("offset", 128, 45, 32, 45, 32), ("outlier", 128, 64, 32, 50, 7), ("offset", 64, 40, 32, 33, 1)])
+def test_delta_exactly_rounded(probe, kind, D, ntiles, tau0, tlim, nrows):
+    """The rank-one term delta[tile][row] = Kbar_tile . q_row of 32 tiles at
+    once, on the FP64 MFMA: the bf16 products are exact in binary64 and so is
+    their sum for these inputs, so every entry must be fl32 of the exact
+    binary64 sum, bit for bit (the offset decides P codes, and the oracle
+    rounds the exact value).  Tiles from tlim on and rows from nrows on give
+    exactly 0, except that a 16-tile half starting at or past tlim is not
+    computed at all (no wave reads it)."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(D + 7 * ntiles + tau0 + nrows)
+    off = rng.standard_normal(D) * 3.0                              # per-channel K offset (the smoothed part)
+    kbar = off[None, :] + 0.3 * rng.standard_normal((ntiles, D))
+    q = rng.standard_normal((32, D)) * 2.0
+    if kind == "outlier":
+        q[:, [3, 70 % D]] *= 20.0
+    kb_bits = oracle.bf16_from_double_array(kbar).reshape(kbar.shape)
+    q_bits = oracle.bf16_from_double_array(q).reshape(q.shape)
+    kb_v, q_v = oracle.bf16_to_f64(kb_bits), oracle.bf16_to_f64(q_bits)
+    kt = torch.from_numpy(np.ascontiguousarray(kb_bits).view(np.int16)).to(dev)
+    qt = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).to(dev)
+    out = torch.full((32, 32), float("nan"), dtype=torch.float32, device=dev)
+    say("delta %s D%d tiles %d tau0 %d tlim %d rows %d" % (kind, D, ntiles, tau0, tlim, nrows))
+    rc = probe.probe_delta(kt.data_ptr(), tlim, tau0, qt.data_ptr(), D, nrows, D, out.data_ptr())
+    assert rc == 0, rc
+    torch.cuda.synchronize()
+    got = to_np(out).astype(np.float64)                             # [tile][row]
+    nt, nr = min(32, tlim - tau0), nrows
+    exact = kb_v[tau0:tau0 + nt] @ q_v[:nr].T                       # bf16 products: exact in binary64
+    written = 16 if nt <= 16 else 32                                # tile halves the call computes
+    assert np.all(got[nt:written, :] == 0.0) and np.all(got[:written, nr:] == 0.0), "past tlim / nrows: not 0"
+    want = exact.astype(np.float32).astype(np.float64)
+    bad = int(np.sum(got[:nt, :nr] != want))
+    say("delta %s D%d: %d of %d entries differ from fl32(exact)" % (kind, D, bad, want.size))
+    assert bad == 0, np.abs(got[:nt, :nr] - want).max()
 
 
 @pytest.mark.parametrize("D,lens", [(64, [5, 517, 129, 1]), (128, [517, 5, 255, 130])])
