@@ -253,6 +253,51 @@ def _decode_oracle_smooth(q, k, v, rows, splits, kv_lens, pv=oracle.PV_FP8):
     return out
 
 
+def _random_prefill_case(i):
+    """Seeded random prefill shape: GQA ratio, odd lengths (Sq > Skv too), D,
+    causal, compensation and fused Q drawn independently."""
+    rng = np.random.default_rng(1000 + i)
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 3]))
+    G = int(rng.choice([1, 2, 4, 5, 8]))
+    B = int(rng.choice([1, 2]))
+    Skv = int(rng.integers(1, 900))
+    Sq = int(rng.integers(1, min(Skv + 120, 600)))
+    causal, smooth, fused = (bool(x) for x in rng.integers(0, 2, size=3))
+    koff = 3.0 if smooth else float(rng.choice([0.0, 1.0]))
+    qs = float(rng.choice([1.0, 2.0]))
+    return B, Hkv * G, Hkv, Sq, Skv, D, causal, smooth, fused, koff, qs
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_prefill_random_shapes(i):
+    B, Hq, Hkv, Sq, Skv, D, causal, smooth, fused, koff, qs = _random_prefill_case(i)
+    label = "rand%d B%d H%d/%d S%d/%d D%d causal%d comp%d fused%d" % (i, B, Hq, Hkv, Sq, Skv, D, causal, smooth,
+                                                                    fused)
+    q, k, v = _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed=2000 + i, k_offset=koff, q_scale=qs)
+    _check_prefill(q, k, v, causal, 1.0 / math.sqrt(D), smooth, _all_rows(B, Hq, Sq), label, fused=fused)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_decode_random_shapes(i):
+    """Seeded random decode shape: batch, GQA ratio (up to 40 query heads per KV
+    head, i.e. two row chunks), ragged cache lengths including empty ones, split
+    count (0 = the library's default), D and compensation."""
+    rng = np.random.default_rng(3000 + i)
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 4, 8, 40]))
+    B = int(rng.integers(1, 5))
+    Smax = int(rng.integers(1, 5000))
+    lens = [int(x) for x in rng.integers(0, Smax + 1, size=B)]
+    lens[0] = Smax
+    splits = int(rng.choice([0, 1, 2, 5, 16]))
+    smooth = bool(rng.integers(2))
+    label = "drand%d B%d H%d/%d S%d D%d splits%d comp%d" % (i, B, Hkv * G, Hkv, Smax, D, splits, smooth)
+    q, k, v = _rand_inputs(B, Hkv * G, Hkv, 1, Smax, D, seed=4000 + i, k_offset=3.0 if smooth else 0.0)
+    _check_decode(q, k, v, splits, kv_lens=lens, label=label, smooth=smooth)
+
+
 @pytest.mark.parametrize("splits", [3, 0, 1])
 def test_decode_small_varlen(splits):
     q, k, v = _rand_inputs(3, 8, 2, 1, 1000, 128, seed=11, q_scale=2.0)
