@@ -79,10 +79,7 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
     // (NVFP4 Q/K keeps the add per score)
     constexpr bool SEED = COMP && PV != QK_NVFP4;
     v16f init = v16f{};
-    if (SEED) {
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) init[rr] = d32;
-    }
+    if (SEED) init = offset_block(d32);
     qk_tile<D, PV>(st, lo, buf, s, init);
     softmax_tile<D, COMP && !SEED, PV>(st, s, t, kTile * t + kTile > L, L - 1, d32, pb, pscale);
     pv_tile<D, PV>(st, lo, buf + TL::V_OFF, pb, pscale);

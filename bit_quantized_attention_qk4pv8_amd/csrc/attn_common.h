@@ -543,6 +543,17 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
   }
 }
 
+// Start block of the S^T accumulator for the compensated kernels: the 32 x 32
+// block (key, row) with every entry equal to the row's offset d (this lane's
+// d, lane l holding row l % 32), built on the matrix unit instead of by 16
+// VALU moves.  One FP32 MFMA (v_mfma_f32_32x32x2f32): A = 1 everywhere, B = d
+// at contraction index 0 (lanes 0..31) and 0 at index 1 (lanes 32..63), so
+// entry (key, row) = 1 * d + 1 * 0 = d exactly, infinities included.
+__device__ __forceinline__ v16f offset_block(float d) {
+  const float b = (threadIdx.x & 32) ? 0.0f : d;
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(1.0f, b, v16f{}, 0, 0, 0);
+}
+
 // One K operand block (32 keys x all channels): the A operands of the D/64
 // MFMAs of key block c and their scale bytes (byte k feeds MFMA k).
 template <int D>

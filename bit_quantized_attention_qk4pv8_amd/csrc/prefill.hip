@@ -204,18 +204,14 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
       compute_delta<D>(dl, a.kbar + (size_t)grp * ntk * D, Tw, t, a.qbf + (((size_t)b * a.Hq + h) * Sq + i0) * D, D,
                        Sq - i0);
     // The compensation offset d = fl32(c2 fl32(delta)) of this lane's row and
-    // tile starts the S accumulator, so the exponent argument
+    // tile starts the S accumulator (offset_block), so the exponent argument
     // y = fl32(fl32(d + S'_0) + S'_1) (S'_k: the exact partial product of
     // MFMA k) needs no add per score.  (NVFP4 Q/K, a contrast format on the
     // bf16 MFMA, keeps the add: its register budget has no room for the
     // start value.)
     constexpr bool SEED = COMP && PV != QK_NVFP4;
     v16f init = v16f{};
-    if (SEED) {
-      const float d32 = a.c2 * dl[(t & 31) * 32 + n];
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) init[rr] = d32;
-    }
+    if (SEED) init = offset_block(a.c2 * dl[(t & 31) * 32 + n]);
     __builtin_amdgcn_s_setprio(2);
     // (a wave's last P V also computes a product of whatever K buffer kb_cur
     // holds; that S is never used: one code path keeps the register budget)

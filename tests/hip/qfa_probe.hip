@@ -15,7 +15,8 @@
 //    the kernels' own tile DMA, operand reads and block-scaled FP4 MFMAs
 //    (attn_common.h), written out as binary32 scores.
 //  - probe_s_tile_seeded: the same tile with the S accumulator started at a
-//    per-row offset d[row], as the compensated kernels start it.
+//    per-row offset d[row], built by offset_block as the compensated kernels
+//    build it.
 //  - probe_tile_rowsum: the E4M3-P denominator of two tiles (tile_rowsum on
 //    each 64-key half, then fold_rowsum with each tile's P scale code), for
 //    P operands given in the 32x32x64 B layout of the P V product.
@@ -86,11 +87,7 @@ __global__ void __launch_bounds__(64) k_s_tile(const uint8_t* q4, const uint8_t*
   lo.init();
   v16f s[4];
   v16f init = v16f{};
-  if (d) {
-    const float dn = d[n];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) init[rr] = dn;
-  }
+  if (d) init = offset_block(d[n]);  // as the compensated kernels build it
   qk_tile<D, PV_FP8>(st, lo, smem, s, init);
   const int nk = min(kTile, L - kTile * t);
 #pragma unroll
