@@ -691,8 +691,10 @@ struct NoHook {
 
 // hook(k) runs after the k-th MFMA step (k = 0 .. 2 D/32 + 3), inside the
 // scheduling fences: a place for instructions that should issue while the
-// matrix unit is busy.
-template <int D, int PV, class Hook = NoHook>
+// matrix unit is busy.  KEEP_INIT (a non-zero start block) keeps init live
+// through the S products: otherwise the last block's MFMA takes over init's
+// registers and the result is copied out again (8 v_mov_b64 per tile).
+template <int D, int PV, class Hook = NoHook, bool KEEP_INIT = false>
 __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV>& lo, const uint8_t* vreg,
                                            const POp<PV> (&pb)[2], const int (&pscale)[2], const uint8_t* kreg,
                                            v16f (&s)[4], const v16f& init, const Hook& hook = Hook()) {
@@ -730,6 +732,7 @@ __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV
     hook(NQ + c);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (KEEP_INIT) asm volatile("" ::"v"(init));
   // (the row sums finished during the S products)
   if constexpr (TS) fold_rowsum(st, ts, pscale[0]);
 }

@@ -216,7 +216,8 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
     // (a wave's last P V also computes a product of whatever K buffer kb_cur
     // holds; that S is never used: one code path keeps the register budget)
     if (do_pv) {
-      pv_then_qk<D, PV>(st, lo, vbuf + vb_prev * TL::VREG, pb, pscale, kbuf + kb_cur * TL::KREG, s, init, dma);
+      pv_then_qk<D, PV, decltype(dma), SEED>(st, lo, vbuf + vb_prev * TL::VREG, pb, pscale, kbuf + kb_cur * TL::KREG,
+                                             s, init, dma);
     } else {
 #pragma unroll
       for (int k = 0; k <= SLOTS; ++k) dma(k);
