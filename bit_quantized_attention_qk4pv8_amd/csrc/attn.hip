@@ -48,7 +48,7 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
   // check cuts off -- measured on MI355X -- so a ragged tile reads zeros)
   uint8_t* bufs = smem;
   float* dl = reinterpret_cast<float*>(smem + 2 * TL::STRIDE);
-  TileLoader<D, 1, PV> ld;
+  TileLoader<D, 1, PV, kCpolNT> ld;  // each cached byte is read once: non-temporal loads
   ld.init(a.k4, a.k4s, a.v8, a.v8s, (size_t)bg, Lmax, L, 0);
   LaneOffs<D, PV> lo;
   lo.init();

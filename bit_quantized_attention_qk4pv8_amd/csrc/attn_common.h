@@ -110,8 +110,10 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // the hardware range check (on voffset + inst_offset) zero-fills a ragged last
 // tile and V blocks past the end, no read leaves the slice, and the per-lane
 // voffsets (which carry the LDS swizzle) stay loop-invariant, so issuing a
-// tile costs no VALU work.
-template <int D, int NW, int PV = PV_FP8>
+// tile costs no VALU work.  CPOL is the loads' cache-policy operand: kCpolNT
+// (non-temporal) for a stream whose bytes are read once (the decode), 0 for
+// tiles that other workgroups read again through L2 (the prefill).
+template <int D, int NW, int PV = PV_FP8, int CPOL = 0>
 struct TileLoader {
   using TL = TileLayout<D, PV>;
   static constexpr int VR = v_record<PV>();
@@ -187,11 +189,11 @@ struct TileLoader {
       if (ins < TL::NK) {
         const uint32_t voff = (NW % 2 == 0) ? vkw : ((ins & 1) ? vk1 : vk0);
         const __amdgpu_buffer_rsrc_t r = rsrc_at(kc, kc_bytes, (uint32_t)t * TL::KC + ins * 1024);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(kreg + ins * 1024), 16, voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(kreg + ins * 1024), 16, voff, 0, 0, CPOL);
       } else if (ins < N) {
         const int i = ins - TL::NK;
         const __amdgpu_buffer_rsrc_t r = rsrc_at(ks, ks_bytes, (uint32_t)t * TL::KS_BYTES + i * 256);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(kreg + TL::KC + i * 256), 4, lane * 4, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(kreg + TL::KC + i * 256), 4, lane * 4, 0, 0, CPOL);
       }
     }
   }
@@ -204,10 +206,10 @@ struct TileLoader {
       const int ins = wave + NW * j;
       if (ins < TL::NV) {
         const __amdgpu_buffer_rsrc_t r = rsrc_at(vc, vc_bytes, (uint32_t)t * TL::VC + ins * 1024);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(vreg + ins * 1024), 16, vv, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(vreg + ins * 1024), 16, vv, 0, 0, CPOL);
       } else if (ins < N) {
         const __amdgpu_buffer_rsrc_t r = rsrc_at(vs, vs_bytes, (uint32_t)t * TL::VS_BYTES);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(vreg + TL::VC), 16, lane * 16, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(vreg + TL::VC), 16, lane * 16, 0, 0, CPOL);
       }
     }
   }
@@ -230,12 +232,12 @@ struct TileLoader {
       const int ins = wave + NW * k;
       const bool e = ek && ins < TL::NK;
       const __amdgpu_buffer_rsrc_t r = rsrc_at(kc, e ? kc_bytes : 0u, (uint32_t)tk * TL::KC + (e ? ins : 0) * 1024);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(e ? kreg + ins * 1024 : trash), 16, vkw, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(e ? kreg + ins * 1024 : trash), 16, vkw, 0, 0, CPOL);
     } else if (k < SLOTS) {
       const int ins = wave + NW * (k - KCS);
       const bool e = ev && ins < TL::NV;
       const __amdgpu_buffer_rsrc_t r = rsrc_at(vc, e ? vc_bytes : 0u, (uint32_t)tv * TL::VC + (e ? ins : 0) * 1024);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(e ? vreg + ins * 1024 : trash), 16, vv, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(e ? vreg + ins * 1024 : trash), 16, vv, 0, 0, CPOL);
     }
   }
   // The scale bytes of a tile pair as dword loads of 256 B, one per wave:
@@ -255,7 +257,7 @@ struct TileLoader {
     const uint32_t off = (uint32_t)(isk ? tk * TL::KS_BYTES : tv * TL::VS_BYTES) + i * 256;
     uint8_t* dst = !e ? trash : (isk ? kreg + TL::KC : vreg + TL::VC) + i * 256;
     const __amdgpu_buffer_rsrc_t r = rsrc_at(base, bytes, off);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, lane * 4, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, lane * 4, 0, 0, CPOL);
   }
 
   // Two scale bytes per token (MXFP4, D = 64) with an odd key count: the last

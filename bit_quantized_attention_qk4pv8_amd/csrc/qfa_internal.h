@@ -20,6 +20,10 @@ constexpr int kRows = 32;    // query rows per wave (one 32x32 MFMA column block
 
 // E8M0 code 127 = 1.0
 constexpr int kScaleOne = 127;
+// Cache-policy operand of a buffer load on gfx950: the non-temporal hint
+// (`nt`).  Measured on MI355X: streaming 3.4 GB once through LDS with
+// buffer_load ... lds reads at 6.95 TB/s with it against 6.18 without.
+constexpr int kCpolNT = 2;
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 
