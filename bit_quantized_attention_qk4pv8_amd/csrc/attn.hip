@@ -7,10 +7,19 @@
 // a contiguous run of whole 128-key tiles; its normalised partial O and its
 // LSE go to the caller's workspace, and k_decode_merge combines them:
 // LSE = log sum_s e^{LSE_s},  O = sum_s e^{LSE_s - LSE} O_s.  The tile loop is
-// the same three steps as the prefill (attn_common.h), double-buffered in LDS.
+// the same three steps as the prefill (attn_common.h), over a ring of two or
+// three LDS tiles (decode_ring).
 #include "attn_common.h"
 
 namespace qfa {
+
+// LDS tile ring of the decode: three tiles (two workgroups per CU) for the
+// E4M3-V formats, two (three or more per CU) for MXFP4 V and NVFP4 Q/K, whose
+// decodes need the extra workgroups.  Measured on MI355X with the B64 x 32768
+// decode: 3 tiles 0.760 / 2 tiles 0.754 of 8 TB/s for the method, 0.671 / 0.714
+// for MXFP4 V, 0.623 / 0.729 for NVFP4 Q/K.
+template <int PV>
+constexpr int decode_ring() { return (PV == PV_FP8 || PV == PV_FP8_BLOCKP) ? 3 : 2; }
 
 // Decode: workgroup = one wave = (b, kv head g, row chunk rc, split s); lane row n
 // = query head g*G + 32*rc + n.  Writes normalised partials to the workspace.
@@ -46,23 +55,27 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
   // (no zeroing of the tile buffers: every byte a tile step reads is written by
   // that tile's DMA first, and the DMA writes zeros for the lanes its range
   // check cuts off -- measured on MI355X -- so a ragged tile reads zeros)
+  constexpr int NBD = decode_ring<PV>();  // tile t lives in buffer t % NBD
   uint8_t* bufs = smem;
-  float* dl = reinterpret_cast<float*>(smem + 2 * TL::STRIDE);
+  float* dl = reinterpret_cast<float*>(smem + NBD * TL::STRIDE);
   TileLoader<D, 1, PV, kCpolNT> ld;  // each cached byte is read once: non-temporal loads
   ld.init(a.k4, a.k4s, a.v8, a.v8s, (size_t)bg, Lmax, L, 0);
   LaneOffs<D, PV> lo;
   lo.init();
-  if (t0 < t1) {
-    ld.issue_k(t0, bufs + (t0 & 1) * TL::STRIDE, 0);
-    ld.issue_v(t0, bufs + (t0 & 1) * TL::STRIDE + TL::V_OFF, 0);
+  auto buf_of = [&](int t) { return bufs + (unsigned)t % NBD * TL::STRIDE; };
+  // tiles t0 .. t0+NBD-2 in flight before the loop; then tile t+NBD-1 is
+  // issued while tile t is computed, into the buffer tile t-1 used
+  for (int j = t0; j < t0 + NBD - 1 && j < t1; ++j) {
+    ld.issue_k(j, buf_of(j), 0);
+    ld.issue_v(j, buf_of(j) + TL::V_OFF, 0);
   }
   wait_vmem_all();
-  if (t0 < t1) ld.fixup(t0, bufs + (t0 & 1) * TL::STRIDE);
+  for (int j = t0; j < t0 + NBD - 1 && j < t1; ++j) ld.fixup(j, buf_of(j));
   __syncthreads();
   for (int t = t0; t < t1; ++t) {
-    if (t + 1 < t1) {
-      ld.issue_k(t + 1, bufs + ((t + 1) & 1) * TL::STRIDE, 0);
-      ld.issue_v(t + 1, bufs + ((t + 1) & 1) * TL::STRIDE + TL::V_OFF, 0);
+    if (t + NBD - 1 < t1) {
+      ld.issue_k(t + NBD - 1, buf_of(t + NBD - 1), 0);
+      ld.issue_v(t + NBD - 1, buf_of(t + NBD - 1) + TL::V_OFF, 0);
     }
     float d32 = 0.0f;
     if (COMP) {
@@ -71,7 +84,7 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
                          a.qbf + ((size_t)b * a.Hq + gk * a.G + 32 * rc) * D, D, a.G - 32 * rc);
       d32 = a.c2 * dl[(t & 31) * 32 + n];
     }
-    uint8_t* buf = bufs + (t & 1) * TL::STRIDE;
+    uint8_t* buf = buf_of(t);
     v16f s[4];
     POp<PV> pb[2];
     int pscale[2];
@@ -83,8 +96,15 @@ __global__ void __launch_bounds__(64) k_decode_split(AttnArgs a, int nrc) {
     qk_tile<D, PV>(st, lo, buf, s, init);
     softmax_tile<D, COMP && !SEED, PV>(st, s, t, kTile * t + kTile > L, L - 1, d32, pb, pscale);
     pv_tile<D, PV>(st, lo, buf + TL::V_OFF, pb, pscale);
-    wait_vmem_all();
-    if (t + 1 < t1) ld.fixup(t + 1, bufs + ((t + 1) & 1) * TL::STRIDE);
+    // tile t+1 has landed once only the loads of tile t+2 (issued this
+    // iteration, NBD = 3) may still be outstanding
+    if (NBD == 3 && t + 2 < t1) {
+      static_assert(TL::NINS <= 63, "vmcnt field");
+      __builtin_amdgcn_s_waitcnt((TL::NINS & 15) | 0x0F70 | ((TL::NINS >> 4) << 14));
+    } else {
+      wait_vmem_all();
+    }
+    if (t + 1 < t1) ld.fixup(t + 1, buf_of(t + 1));
     __syncthreads();
   }
   if (!rvalid) return;
@@ -154,7 +174,7 @@ static hipError_t decode_dp(const AttnArgs& a, float* O, float* lse, hipStream_t
   const long long nwg = (long long)a.B * a.Hkv * nrc * a.num_splits;
   if (nwg == 0) return hipSuccess;
   const bool comp = a.kbar != nullptr;
-  const size_t lds = 2 * TL::STRIDE + (comp ? 32 * 32 * 4 : 0);
+  const size_t lds = decode_ring<PV>() * TL::STRIDE + (comp ? 32 * 32 * 4 : 0);
   if (comp)
     hipLaunchKernelGGL((k_decode_split<D, true, PV>), dim3((unsigned)nwg), dim3(64), lds, s, a, nrc);
   else
