@@ -54,7 +54,10 @@
  *    returned in binary64 here, LSE in natural-log units referring to the
  *    compensated logits.
  *  - Rank-one smoothing compensation: K is smoothed per 128-token block by its
- *    channel mean Kbar (rounded to bf16); every logit of a block gets back the
+ *    channel mean Kbar: the block's values of the channel summed in binary64
+ *    in token order (exact unless they span more than 2^38 in magnitude),
+ *    divided by the count of present tokens in binary64, rounded to bf16 (an
+ *    infinite or NaN mean stays one).  Every logit of a block gets back the
  *    rank-one term q_bf16 . Kbar_block.
  *  - Causal masks are bottom-right aligned: key j is visible to query i iff
  *    j <= i + (L - Sq).  Query head h reads kv head h / (Hq / Hkv).
@@ -181,6 +184,7 @@ uint16_t orc_bf16_from_double(double v) {
   uint16_t sign = signbit(v) ? 0x8000 : 0;
   double a = fabs(v);
   if (isnan(v)) return 0x7FC0;
+  if (isinf(v)) return sign | 0x7F80;
   if (a == 0.0) return sign;
   if (a < ldexp(1.0, -126)) { /* subnormal: units of 2^-133 */
     double n = nearbyint(ldexp(a, 133));
@@ -200,9 +204,11 @@ uint16_t orc_bf16_from_double(double v) {
 /* Quantizers                                                                */
 /* ------------------------------------------------------------------------- */
 
-/* Channel means of K per 128-token block, from an exact binary64 sum, divided
- * by the count of present tokens and rounded to bf16.
- * kbar layout [B][H][ceil(S/128)][D]. */
+/* Channel means of K per 128-token block: the binary64 sum in token order
+ * (exact while the block's values of the channel span at most 2^38 in
+ * magnitude: then every partial sum is an integer multiple of the smallest
+ * value's bf16 unit below 2^53 of them), divided by the count of present
+ * tokens and rounded to bf16.  kbar layout [B][H][ceil(S/128)][D]. */
 static void kbar_of(const uint16_t* x, int64_t S, int64_t D, uint16_t* kbar) {
   int64_t nt = (S + QFA_ORC_TILE - 1) / QFA_ORC_TILE;
   for (int64_t t = 0; t < nt; ++t) {

@@ -132,6 +132,15 @@ def test_bf16_rounding_matches_torch():
     bits = np.array([0x3F80, 0xBF80, 0x0001, 0x7F7F, 0x4049], np.uint16)
     ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     assert [oracle.bf16_value(int(b)) for b in bits] == list(ref)
+    # infinities and overflow: the largest finite bf16 is 0x7F7F = (2 - 2^-7) 2^127;
+    # from the midpoint (2 - 2^-8) 2^127 on, values round to infinity (ties to even)
+    big = np.array([np.inf, -np.inf, 3.3895e38, 3.3961776e38, 3.3961775e38, -3.4e38,
+                    np.finfo(np.float32).max], np.float32)
+    ref = torch.from_numpy(big).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    mine = oracle.bf16_from_double_array(big.astype(np.float64))
+    assert (mine == ref).all(), (mine, ref)
+    assert oracle.bf16_from_double(1e300) == 0x7F80 and oracle.bf16_from_double(-1e300) == 0xFF80
+    assert oracle.bf16_from_double(float("nan")) == 0x7FC0
 
 
 # --------------------------------------------------------------------------- E8M0 / scale rule
@@ -283,6 +292,32 @@ def test_kbar_is_nearest_bf16_of_exact_mean():
     c2, s2, kb2 = oracle.quantize_qk4(b2, smooth=True)
     assert (kb2[0, 0, 0] == b2[0, 0, 0]).all()
     assert (s2 == 0).all() and ((c2 & 0x77) == 0).all()
+
+
+def test_kbar_nonfinite_and_order():
+    """Kbar of blocks holding infinities or NaN is the IEEE mean (inf, -inf or
+    NaN), and the smoothed blocks of that channel are non-finite (scale 0xFF,
+    zero codes).  The sum runs in token order: a channel whose values span
+    more than binary64 adds exactly keeps the token-order rounding."""
+    D = 64
+    k = np.ones((1, 1, 128, D), np.float32)
+    k[0, 0, 3, 0] = np.inf                        # -> +inf
+    k[0, 0, 4, 1] = -np.inf                       # -> -inf
+    k[0, 0, 5, 2], k[0, 0, 6, 2] = np.inf, -np.inf  # -> NaN
+    k[0, 0, 7, 3] = np.nan                        # -> NaN
+    k[0, 0, 0, 32], k[0, 0, 64, 32] = 2.0**60, -(2.0**60)   # token order: 2^60 + 1 = 2^60
+    bits = torch.from_numpy(k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    codes, scales, kbar = oracle.quantize_qk4(bits, smooth=True)
+    kb = kbar[0, 0, 0]
+    assert kb[0] == 0x7F80 and kb[1] == 0xFF80
+    assert (kb[2] & 0x7FFF) > 0x7F80 and (kb[3] & 0x7FFF) > 0x7F80
+    assert (kb[4:32] == 0x3F80).all()                  # mean of ones
+    # rows 1..63 add 1 to 2^60 and are lost; from row 64 on the sum restarts at 0
+    assert oracle.bf16_value(int(kb[32])) == 63.0 / 128.0
+    assert (scales[0, 0, :, 0] == 0xFF).all() and (codes[0, 0, :, :16] == 0).all()
+    assert (scales[0, 0, :, 1] != 0xFF).all()
+    nv_codes, nv_scales, nv_kbar = oracle.quantize_nvfp4(bits, 1.0, smooth=True)
+    assert (nv_kbar == kbar).all()
 
 
 def test_v4_quantizer_bruteforce_vs_printed_table():
