@@ -9,8 +9,9 @@
 //  * Q is multiplied by c2 = fl32(softmax_scale * log2 e) in binary32 first
 //    (prescale), so that Q'K^T is the softmax exponent in log2 units.
 //  * K smoothing for the rank-one compensation: per 128-token block channel
-//    means, summed exactly in binary64, divided by the number of present tokens
-//    and rounded to bf16; the quantised tensor is fl32(K - Kbar).
+//    means, the binary64 sum in token order (exact unless the values span more
+//    than 2^38 in magnitude), divided by the number of present tokens and
+//    rounded to bf16; the quantised tensor is fl32(K - Kbar).
 //  * V -> E4M3 with one E8M0 scale per 32 consecutive tokens of one channel
 //    (exponent ceil(log2 amax) - 8), stored block-contiguous [.., S/32, D, 32].
 //
@@ -39,6 +40,86 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
   return sign | (uint16_t)((ex << 7) | man);
 }
 
+// K-bar of one 128-token tile: for each channel c, bf16_RNE(s_c / n) with
+// s_c = sum_j x[j][c] over the tile's n present rows, accumulated in binary64
+// in row order.  Run by the workgroup's 256 threads: with RG = 256 / (D/8)
+// row groups, thread t < RG * D/8 reads the 16-byte chunk t % (D/8) (8
+// channels) of rows t / (D/8), + RG, ... (coalesced, all loads in flight
+// together) and keeps 8 partial sums, which meet in red (LDS, RG * D <= 2048
+// doubles).  A different order of the additions
+// gives the same s_c whenever every partial sum is exact: a bf16 value with
+// exponent field E >= 1 is an integer multiple of 2^(E-134) below 2^(E-126)
+// (subnormals: multiples of 2^-133), so a sum of at most 128 of them whose
+// nonzero exponent fields lie within E_min..E_max is an integer multiple of
+// 2^(max(E_min,1)-134) below 2^(E_max-119), exact in binary64 while
+// E_max - max(E_min,1) <= 38.  The tile-wide exponent range is tracked on the
+// way; a tile outside it (or holding an infinity or a NaN) is summed again in
+// row order by thread c.  Writes kb[c] (binary32) and kbar_out[c] (bf16 bits);
+// ends with the workgroup synchronised.  row(j) gives row j's first element.
+template <int D, class Row>
+__device__ __forceinline__ void tile_kbar(const Row& row, int n, float* kb, uint16_t* kbar_out, double* red,
+                                          uint32_t* erange) {
+  constexpr int CH = D / 8;                   // 16-byte chunks per row
+  constexpr int RG = 256 / CH;                // row groups (threads from RG * CH on only reduce)
+  constexpr int PER = (kTile + RG - 1) / RG;  // rows per thread
+  static_assert(D % 8 == 0 && CH <= 256 && RG * D <= 2048, "row groups");
+  const int t = threadIdx.x, ch = t % CH, rg = t / CH;
+  const bool act = rg < RG;
+  uint4 u[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = rg + i * RG;
+    u[i] = (act && j < n) ? *reinterpret_cast<const uint4*>(row(j) + 8 * ch) : uint4{0u, 0u, 0u, 0u};
+  }
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  uint32_t amax = 0u, amin = 0x7FFFu;  // largest / smallest nonzero magnitude bits
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t wds[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t h = (k & 1) ? (wds[k >> 1] >> 16) : (wds[k >> 1] & 0xFFFFu);
+      const uint32_t m = h & 0x7FFFu;
+      amax = max(amax, m);
+      amin = min(amin, m ? m : 0x7FFFu);
+      acc[k] += (double)bf16_bits_to_float(h);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
+    amin = min(amin, (uint32_t)__shfl_xor((int)amin, o));
+  }
+  if ((t & 63) == 0) {
+    erange[2 * (t >> 6)] = amax;
+    erange[2 * (t >> 6) + 1] = amin;
+  }
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[rg * D + 8 * ch + i] = acc[i];
+  }
+  __syncthreads();
+  if (t < D) {
+    uint32_t mx = 0u, mn = 0x7FFFu;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mx = max(mx, erange[2 * w]);
+      mn = min(mn, erange[2 * w + 1]);
+    }
+    const int emax = (int)(mx >> 7), emin = max((int)(mn >> 7), 1);
+    double sum = 0.0;
+    if (emax - emin <= 38) {
+      for (int r = 0; r < RG; ++r) sum += red[r * D + t];
+    } else {
+      for (int j = 0; j < n; ++j) sum += (double)bf16_bits_to_float(row(j)[t]);
+    }
+    const uint16_t b = f64_to_bf16_rne(sum / (double)n);
+    kb[t] = bf16_bits_to_float(b);
+    kbar_out[t] = b;
+  }
+  __syncthreads();
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) k_quant_qk4(const uint16_t* __restrict__ x, int S, int ntiles, int smooth,
                                                    float prescale, uint8_t* __restrict__ codes,
@@ -51,14 +132,9 @@ __global__ void __launch_bounds__(256) k_quant_qk4(const uint16_t* __restrict__ 
   const int n = min(kTile, S - t0);
   const uint16_t* xs = x + (bh * (size_t)S + t0) * D;
   if (smooth) {
-    for (int c = threadIdx.x; c < D; c += blockDim.x) {
-      double sum = 0.0;
-      for (int j = 0; j < n; ++j) sum += (double)bf16_bits_to_float(xs[(size_t)j * D + c]);
-      uint16_t b = f64_to_bf16_rne(sum / (double)n);
-      kb[c] = bf16_bits_to_float(b);
-      kbar[(bh * ntiles + tile) * D + c] = b;
-    }
-    __syncthreads();
+    __shared__ double red[256 * 8];
+    __shared__ uint32_t erange[8];
+    tile_kbar<D>([&](int j) { return xs + (size_t)j * D; }, n, kb, kbar + (bh * ntiles + tile) * D, red, erange);
   }
   for (int w = threadIdx.x; w < n * NB; w += blockDim.x) {
     const int j = w / NB, blk = w % NB;
@@ -95,14 +171,9 @@ __global__ void __launch_bounds__(256) k_quant_nvfp4(const uint16_t* __restrict_
   const int n = min(kTile, S - t0);
   const uint16_t* xs = x + (bh * (size_t)S + t0) * D;
   if (smooth) {
-    for (int c = threadIdx.x; c < D; c += blockDim.x) {
-      double sum = 0.0;
-      for (int j = 0; j < n; ++j) sum += (double)bf16_bits_to_float(xs[(size_t)j * D + c]);
-      uint16_t b = f64_to_bf16_rne(sum / (double)n);
-      kb[c] = bf16_bits_to_float(b);
-      kbar[(bh * ntiles + tile) * D + c] = b;
-    }
-    __syncthreads();
+    __shared__ double red[256 * 8];
+    __shared__ uint32_t erange[8];
+    tile_kbar<D>([&](int j) { return xs + (size_t)j * D; }, n, kb, kbar + (bh * ntiles + tile) * D, red, erange);
   }
   for (int w = threadIdx.x; w < n * NB; w += blockDim.x) {
     const int j = w / NB, blk = w % NB;
@@ -284,14 +355,10 @@ __global__ void __launch_bounds__(256) k_append_k(AppendArgs a, int smooth) {
   const int lo = smooth ? t0 : max(t0, L);
   if (smooth) {
     const size_t ntiles = (size_t)(a.S + kTile - 1) / kTile;
-    for (int c = threadIdx.x; c < D; c += blockDim.x) {
-      double sum = 0.0;
-      for (int j = 0; j < np; ++j) sum += (double)bf16_bits_to_float(tok_row<D>(a.k_tail, a.k_new, bg, a.n, L, t0 + j)[c]);
-      const uint16_t bb = f64_to_bf16_rne(sum / (double)np);
-      kb[c] = bf16_bits_to_float(bb);
-      a.kbar[(bg * ntiles + tile) * D + c] = bb;
-    }
-    __syncthreads();
+    __shared__ double red[256 * 8];
+    __shared__ uint32_t erange[8];
+    tile_kbar<D>([&](int j) { return tok_row<D>(a.k_tail, a.k_new, bg, a.n, L, t0 + j); }, np, kb,
+                 a.kbar + (bg * ntiles + tile) * D, red, erange);
   }
   const int nrows = t0 + np - lo;
   if (a.k_nv_g > 0.0f) {  // NVFP4 rows (blocks of 16, E4M3 scales)

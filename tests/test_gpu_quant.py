@@ -111,6 +111,53 @@ def test_quantizers_nonfinite_and_tiny():
     _check_v8(xb, "nonfinite")
     _check_v4(xb, "nonfinite")
     _check_nvfp4(xb, False, "nonfinite")
+    _check_qk4(xb, True, "nonfinite.smooth")
+    _check_nvfp4(xb, True, "nonfinite.smooth")
+
+
+def _row_order_vs_grouped(col: np.ndarray, groups: int):
+    """Binary64 sums of one channel of one tile: in row order, and as `groups`
+    strided partial sums added up afterwards."""
+    seq = 0.0
+    for v in col:
+        seq += float(v)
+    parts = [0.0] * groups
+    for j, v in enumerate(col):
+        parts[j % groups] += float(v)
+    tot = 0.0
+    for p in parts:
+        tot += p
+    return seq, tot
+
+
+@pytest.mark.parametrize("D", [64, 96, 128, 256])
+def test_kbar_order_sensitive_tiles(D):
+    """K-bar is the row-order binary64 sum also where the order changes the
+    result (a tile whose values span more exponents than binary64 adds
+    exactly), next to tiles that sum exactly (wide but bounded range), hold
+    an infinity or a NaN, or mix subnormals with normal values."""
+    rng = np.random.default_rng(D)
+    x = rng.standard_normal((1, 2, 300, D)).astype(np.float32)
+    col = np.ones(128, np.float32)
+    col[0], col[64] = 2.0 ** 60, -(2.0 ** 60)
+    x[0, 0, :128, 0] = col
+    seq, grouped = _row_order_vs_grouped(col, 256 // (D // 8))
+    assert seq != grouped  # the case is order sensitive
+    x[0, 0, :128, 1] = -col
+    # exponents within 38 of each other: exact in any order
+    e = rng.integers(-19, 20, size=(128, D))
+    x[0, 0, 128:256] = (np.ldexp(1.0, e) * rng.uniform(1.0, 2.0, (128, D)) * rng.choice([-1.0, 1.0], (128, D))
+                        ).astype(np.float32)
+    x[0, 0, 260, 3] = np.inf
+    x[0, 0, 270, 4] = np.nan
+    x[0, 0, 280:290, 5] = -np.inf
+    x[0, 0, 281, 6], x[0, 0, 282, 6] = np.inf, -np.inf
+    x[0, 1, :128, :8] = 1e-39                    # bf16 subnormals beside normal values
+    x[0, 1, 3, :8] = 3.0
+    x[0, 1, 128:256, 9] = 3.0e38                 # sums past the bf16 range
+    xb = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    _check_qk4(xb, True, "kbar-order D%d" % D)
+    _check_nvfp4(xb, True, "kbar-order D%d" % D)
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama16k", "qwen32k"])
