@@ -341,6 +341,138 @@ struct RowState {
 template <int PV>
 using POp = typename std::conditional<pv_of(PV) == PV_FP4, v4i, v8i>::type;
 
+// ---- O^T in fixed accumulation registers (method prefill, no compensation)
+// In that kernel O^T lives in AGPRs a0 .. a(D/2 - 1), block cb in
+// a[16 cb .. 16 cb + 15], and only inline assembly touches it: the P V MFMAs
+// accumulate there, the rare frame rebase and the epilogue go through
+// v_accvgpr_read/write.  (The MFMA builtins pick one register file for every
+// MFMA of a kernel, and S has to stay in VGPRs for the softmax.)  With O in
+// AGPRs an MFMA issue holds back the other wave's VALU work for fewer cycles:
+// llama16k measured 4% faster on MI355X.
+// The compiler does not know these registers hold a value between the
+// statements, so the kernel is correct only while the compiler allocates no
+// AGPR of its own in it; a test compiles the kernel and checks exactly that
+// (it needs about 124 VGPRs, inside the 128 the compiler keeps for VGPRs in a
+// kernel that uses AGPRs).  Hazards the compiler cannot see: VALU code reads
+// or rewrites O only after ofix_settle (24 wait states, more than a 16-pass
+// MFMA's result needs); two MFMAs on one block are four MFMAs apart; the P, V
+// and scale operands come from LDS loads (which the compiler's waits cover) or
+// from VALU writes a whole softmax phase before the MFMA.
+__device__ __forceinline__ void ofix_settle() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 7");
+#endif
+}
+// O^T block cb += V^T P^T (E4M3 x E4M3 with block scales sa, sb).
+__device__ __forceinline__ void ofix_mfma(int cb, const v8i& a, const v8i& b, int sa, int sb) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  switch (cb) {
+    case 0:
+      asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 a[0:15], %0, %1, a[0:15], %2, %3 op_sel_hi:[0,0,0]"
+                   :
+                   : "v"(a), "v"(b), "v"(sa), "v"(sb)
+                   : "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15");
+      break;
+    case 1:
+      asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 a[16:31], %0, %1, a[16:31], %2, %3 op_sel_hi:[0,0,0]"
+                   :
+                   : "v"(a), "v"(b), "v"(sa), "v"(sb)
+                   : "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31");
+      break;
+    case 2:
+      asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 a[32:47], %0, %1, a[32:47], %2, %3 op_sel_hi:[0,0,0]"
+                   :
+                   : "v"(a), "v"(b), "v"(sa), "v"(sb)
+                   : "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47");
+      break;
+    case 3:
+      asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 a[48:63], %0, %1, a[48:63], %2, %3 op_sel_hi:[0,0,0]"
+                   :
+                   : "v"(a), "v"(b), "v"(sa), "v"(sb)
+                   : "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63");
+      break;
+  }
+#endif
+}
+#if defined(__HIP_DEVICE_COMPILE__)
+#define QFA_OFIX_Z(N) asm volatile("v_accvgpr_write_b32 a" #N ", 0" ::: "a" #N)
+#define QFA_OFIX_RD(N) asm volatile("v_accvgpr_read_b32 %0, a" #N : "=v"(x[N]))
+#define QFA_OFIX_SC(N)                                                                                  \
+  asm volatile("v_accvgpr_read_b32 %0, a" #N "\n v_mul_f32 %0, %0, %1\n v_accvgpr_write_b32 a" #N ", %0" \
+               : "=&v"(t)                                                                               \
+               : "v"(f)                                                                                 \
+               : "a" #N)
+#else
+#define QFA_OFIX_Z(N)
+#define QFA_OFIX_RD(N) x[N] = 0.0f
+#define QFA_OFIX_SC(N) (void)t
+#endif
+// O^T = 0 for the first NB blocks (plain AGPR writes: an MFMA would read
+// operands the compiler does not know are read).
+template <int NB>
+__device__ __forceinline__ void ofix_zero() {
+  if constexpr (NB > 0) {
+    QFA_OFIX_Z(0); QFA_OFIX_Z(1); QFA_OFIX_Z(2); QFA_OFIX_Z(3); QFA_OFIX_Z(4); QFA_OFIX_Z(5); QFA_OFIX_Z(6); QFA_OFIX_Z(7);
+    QFA_OFIX_Z(8); QFA_OFIX_Z(9); QFA_OFIX_Z(10); QFA_OFIX_Z(11); QFA_OFIX_Z(12); QFA_OFIX_Z(13); QFA_OFIX_Z(14); QFA_OFIX_Z(15);
+  }
+  if constexpr (NB > 1) {
+    QFA_OFIX_Z(16); QFA_OFIX_Z(17); QFA_OFIX_Z(18); QFA_OFIX_Z(19); QFA_OFIX_Z(20); QFA_OFIX_Z(21); QFA_OFIX_Z(22); QFA_OFIX_Z(23);
+    QFA_OFIX_Z(24); QFA_OFIX_Z(25); QFA_OFIX_Z(26); QFA_OFIX_Z(27); QFA_OFIX_Z(28); QFA_OFIX_Z(29); QFA_OFIX_Z(30); QFA_OFIX_Z(31);
+  }
+  if constexpr (NB > 2) {
+    QFA_OFIX_Z(32); QFA_OFIX_Z(33); QFA_OFIX_Z(34); QFA_OFIX_Z(35); QFA_OFIX_Z(36); QFA_OFIX_Z(37); QFA_OFIX_Z(38); QFA_OFIX_Z(39);
+    QFA_OFIX_Z(40); QFA_OFIX_Z(41); QFA_OFIX_Z(42); QFA_OFIX_Z(43); QFA_OFIX_Z(44); QFA_OFIX_Z(45); QFA_OFIX_Z(46); QFA_OFIX_Z(47);
+  }
+  if constexpr (NB > 3) {
+    QFA_OFIX_Z(48); QFA_OFIX_Z(49); QFA_OFIX_Z(50); QFA_OFIX_Z(51); QFA_OFIX_Z(52); QFA_OFIX_Z(53); QFA_OFIX_Z(54); QFA_OFIX_Z(55);
+    QFA_OFIX_Z(56); QFA_OFIX_Z(57); QFA_OFIX_Z(58); QFA_OFIX_Z(59); QFA_OFIX_Z(60); QFA_OFIX_Z(61); QFA_OFIX_Z(62); QFA_OFIX_Z(63);
+  }
+}
+// x[16 cb + rr] = O^T block cb, element rr.
+template <int NB>
+__device__ __forceinline__ void ofix_read(float (&x)[64]) {
+  if constexpr (NB > 0) {
+    QFA_OFIX_RD(0); QFA_OFIX_RD(1); QFA_OFIX_RD(2); QFA_OFIX_RD(3); QFA_OFIX_RD(4); QFA_OFIX_RD(5); QFA_OFIX_RD(6); QFA_OFIX_RD(7);
+    QFA_OFIX_RD(8); QFA_OFIX_RD(9); QFA_OFIX_RD(10); QFA_OFIX_RD(11); QFA_OFIX_RD(12); QFA_OFIX_RD(13); QFA_OFIX_RD(14); QFA_OFIX_RD(15);
+  }
+  if constexpr (NB > 1) {
+    QFA_OFIX_RD(16); QFA_OFIX_RD(17); QFA_OFIX_RD(18); QFA_OFIX_RD(19); QFA_OFIX_RD(20); QFA_OFIX_RD(21); QFA_OFIX_RD(22); QFA_OFIX_RD(23);
+    QFA_OFIX_RD(24); QFA_OFIX_RD(25); QFA_OFIX_RD(26); QFA_OFIX_RD(27); QFA_OFIX_RD(28); QFA_OFIX_RD(29); QFA_OFIX_RD(30); QFA_OFIX_RD(31);
+  }
+  if constexpr (NB > 2) {
+    QFA_OFIX_RD(32); QFA_OFIX_RD(33); QFA_OFIX_RD(34); QFA_OFIX_RD(35); QFA_OFIX_RD(36); QFA_OFIX_RD(37); QFA_OFIX_RD(38); QFA_OFIX_RD(39);
+    QFA_OFIX_RD(40); QFA_OFIX_RD(41); QFA_OFIX_RD(42); QFA_OFIX_RD(43); QFA_OFIX_RD(44); QFA_OFIX_RD(45); QFA_OFIX_RD(46); QFA_OFIX_RD(47);
+  }
+  if constexpr (NB > 3) {
+    QFA_OFIX_RD(48); QFA_OFIX_RD(49); QFA_OFIX_RD(50); QFA_OFIX_RD(51); QFA_OFIX_RD(52); QFA_OFIX_RD(53); QFA_OFIX_RD(54); QFA_OFIX_RD(55);
+    QFA_OFIX_RD(56); QFA_OFIX_RD(57); QFA_OFIX_RD(58); QFA_OFIX_RD(59); QFA_OFIX_RD(60); QFA_OFIX_RD(61); QFA_OFIX_RD(62); QFA_OFIX_RD(63);
+  }
+}
+// O^T *= f.
+template <int NB>
+__device__ __forceinline__ void ofix_scale(float f) {
+  float t = 0.0f;
+  if constexpr (NB > 0) {
+    QFA_OFIX_SC(0); QFA_OFIX_SC(1); QFA_OFIX_SC(2); QFA_OFIX_SC(3); QFA_OFIX_SC(4); QFA_OFIX_SC(5); QFA_OFIX_SC(6); QFA_OFIX_SC(7);
+    QFA_OFIX_SC(8); QFA_OFIX_SC(9); QFA_OFIX_SC(10); QFA_OFIX_SC(11); QFA_OFIX_SC(12); QFA_OFIX_SC(13); QFA_OFIX_SC(14); QFA_OFIX_SC(15);
+  }
+  if constexpr (NB > 1) {
+    QFA_OFIX_SC(16); QFA_OFIX_SC(17); QFA_OFIX_SC(18); QFA_OFIX_SC(19); QFA_OFIX_SC(20); QFA_OFIX_SC(21); QFA_OFIX_SC(22); QFA_OFIX_SC(23);
+    QFA_OFIX_SC(24); QFA_OFIX_SC(25); QFA_OFIX_SC(26); QFA_OFIX_SC(27); QFA_OFIX_SC(28); QFA_OFIX_SC(29); QFA_OFIX_SC(30); QFA_OFIX_SC(31);
+  }
+  if constexpr (NB > 2) {
+    QFA_OFIX_SC(32); QFA_OFIX_SC(33); QFA_OFIX_SC(34); QFA_OFIX_SC(35); QFA_OFIX_SC(36); QFA_OFIX_SC(37); QFA_OFIX_SC(38); QFA_OFIX_SC(39);
+    QFA_OFIX_SC(40); QFA_OFIX_SC(41); QFA_OFIX_SC(42); QFA_OFIX_SC(43); QFA_OFIX_SC(44); QFA_OFIX_SC(45); QFA_OFIX_SC(46); QFA_OFIX_SC(47);
+  }
+  if constexpr (NB > 3) {
+    QFA_OFIX_SC(48); QFA_OFIX_SC(49); QFA_OFIX_SC(50); QFA_OFIX_SC(51); QFA_OFIX_SC(52); QFA_OFIX_SC(53); QFA_OFIX_SC(54); QFA_OFIX_SC(55);
+    QFA_OFIX_SC(56); QFA_OFIX_SC(57); QFA_OFIX_SC(58); QFA_OFIX_SC(59); QFA_OFIX_SC(60); QFA_OFIX_SC(61); QFA_OFIX_SC(62); QFA_OFIX_SC(63);
+  }
+}
+#undef QFA_OFIX_Z
+#undef QFA_OFIX_RD
+#undef QFA_OFIX_SC
+
 // Softmax step of one tile.  s holds S' = Q'K^T, the logits in log2 units
 // (Q carries the factor softmax_scale * log2 e).  Masks keys > jlim (when
 // need_mask), adds the compensation offset d32 = fl32(c2 * delta) (COMP),
@@ -350,7 +482,7 @@ using POp = typename std::conditional<pv_of(PV) == PV_FP4, v4i, v8i>::type;
 // 2^(m - m_ref) (PV_FP8), or 2^(e_b - m_ref) of the key block b = 2h + g
 // whose scale this lane supplies (PV_FP8_BLOCKP, PV_FP4).  O and l are
 // touched only by the rare frame rebase.
-template <int D, bool COMP, int PV>
+template <int D, bool COMP, int PV, bool OF = false>
 __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int t, bool need_mask, int jlim,
                                              float d32, POp<PV> (&pb)[2], int (&pscale)[2]) {
   constexpr int P = pv_of(PV);
@@ -447,10 +579,15 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, v16f (&s)[4], int 
   // past 2^64 (rare: the row max would have to climb 64 binades).
   if (__builtin_amdgcn_ballot_w64(mn - st.m_ref > 64.0f)) {
     const float f = (mn - st.m_ref > 64.0f) ? __builtin_ldexpf(1.0f, (int)(st.m_ref - mn)) : 1.0f;
+    if constexpr (OF) {
+      ofix_settle();
+      ofix_scale<D / 32>(f);
+    } else {
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+      for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(st.o[cb][rr]) : "v"(f));
+        for (int rr = 0; rr < 16; ++rr) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(st.o[cb][rr]) : "v"(f));
+    }
     if constexpr (P == PV_FP8) {
       st.lsum *= f;
     } else {
@@ -655,6 +792,15 @@ __device__ __forceinline__ POp<PV> ones_op(const v8i& ones) {
     return ones;
 }
 
+// O^T block cb += V^T P^T, in VGPRs or (OF) in the fixed accumulation registers.
+template <int D, int PV, bool OF>
+__device__ __forceinline__ void o_acc(RowState<D>& st, int cb, const POp<PV>& a, const POp<PV>& b, int sa, int sb) {
+  if constexpr (OF)
+    ofix_mfma(cb, a, b, sa, sb);
+  else
+    st.o[cb] = mfma_pv<PV>(a, b, st.o[cb], sa, sb);
+}
+
 // Row sums of the E4M3 P codes of one 64-key half, accumulated into ts, on
 // one 16x16x128 MFMA at unit scales.  Read as the B operand of that product,
 // the 32x32x64 P operand pb (lane l: query l % 32) gives output column c the
@@ -696,7 +842,7 @@ struct NoHook {
 // matrix unit is busy.  KEEP_INIT (a non-zero start block) keeps init live
 // through the S products: otherwise the last block's MFMA takes over init's
 // registers and the result is copied out again (8 v_mov_b64 per tile).
-template <int D, int PV, class Hook = NoHook, bool KEEP_INIT = false>
+template <int D, int PV, class Hook = NoHook, bool KEEP_INIT = false, bool OF = false>
 __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV>& lo, const uint8_t* vreg,
                                            const POp<PV> (&pb)[2], const int (&pscale)[2], const uint8_t* kreg,
                                            v16f (&s)[4], const v16f& init, const Hook& hook = Hook()) {
@@ -713,7 +859,7 @@ __device__ __forceinline__ void pv_then_qk(RowState<D>& st, const LaneOffs<D, PV
   for (int q = 0; q < NQ; ++q) {
     __builtin_amdgcn_sched_barrier(0);
     const int h = q / (D / 32), cb = q % (D / 32);
-    st.o[cb] = mfma_pv<PV>(va[q % R], pb[h], st.o[cb], vs[q % R], pscale[h]);
+    o_acc<D, PV, OF>(st, cb, va[q % R], pb[h], vs[q % R], pscale[h]);
     if (cb == D / 32 - 1) {
       if constexpr (TS)
         ts = tile_rowsum(st.sel, pb[h], ts);
@@ -755,7 +901,7 @@ __device__ __forceinline__ void pv_tile(RowState<D>& st, const LaneOffs<D, PV>& 
   for (int q = 0; q < NQ; ++q) {
     __builtin_amdgcn_sched_barrier(0);
     const int h = q / (D / 32), cb = q % (D / 32);
-    st.o[cb] = mfma_pv<PV>(va[q % R], pb[h], st.o[cb], vs[q % R], pscale[h]);
+    o_acc<D, PV, false>(st, cb, va[q % R], pb[h], vs[q % R], pscale[h]);
     if (cb == D / 32 - 1) {
       if constexpr (TS)
         ts = tile_rowsum(st.sel, pb[h], ts);
@@ -787,16 +933,26 @@ __device__ __forceinline__ void qk_tile(const RowState<D>& st, const LaneOffs<D,
 // Epilogue of one row: O = O^T / l (this lane writes half of the row's
 // channels) and LSE = ln2 * (m_ref + log2(l / 256)) (E4M3 P: codes of
 // 256 * 2^(y - e); E2M1 P: 4 * 2^(y - e), so l / 4).  lse_row may be null.
-template <int D, int PV = PV_FP8>
+template <int D, int PV = PV_FP8, bool OF = false>
 __device__ __forceinline__ void store_row(const RowState<D>& st, float* orow, float* lse_row) {
   const int g = (threadIdx.x & 63) >> 5;
   const float l = pv_of(PV) == PV_FP8 ? st.lsum : st.lv[0];
   const bool empty = (st.m == -__builtin_inff());
   const float inv = empty ? 0.0f : 1.0f / l;
+  if constexpr (OF) {
+    float x[64];
+    ofix_settle();
+    ofix_read<D / 32>(x);
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb)
+    for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) orow[32 * cb + (rr >> 2) * 8 + 4 * g + (rr & 3)] = st.o[cb][rr] * inv;
+      for (int rr = 0; rr < 16; ++rr) orow[32 * cb + (rr >> 2) * 8 + 4 * g + (rr & 3)] = x[16 * cb + rr] * inv;
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) orow[32 * cb + (rr >> 2) * 8 + 4 * g + (rr & 3)] = st.o[cb][rr] * inv;
+  }
   if (lse_row && g == 0)
     *lse_row = empty ? -__builtin_inff()
                      : 0.69314718055994531f * (st.m_ref + __builtin_log2f(l * (PV == PV_FP4 ? 0x1p-2f : 0x1p-8f)));
@@ -867,7 +1023,7 @@ __device__ __forceinline__ void compute_delta(float* dl, const uint16_t* kbar_bg
 // (times c2, then the MXFP4 block rule): the same bytes the quantiser kernel
 // writes for Q with prescale c2.  QK_NVFP4 takes the quantised row (codes, E4M3
 // scales) and the tensor scales gq, gk, and keeps Q as bf16.
-template <int D, int PV = PV_FP8>
+template <int D, int PV = PV_FP8, bool OF = false>
 __device__ __forceinline__ void load_q(RowState<D>& st, const uint8_t* q4row, const uint8_t* q4srow,
                                        const uint16_t* qbfrow, float c2, bool valid, float gq = 1.0f,
                                        float gk = 1.0f) {
@@ -906,8 +1062,12 @@ __device__ __forceinline__ void load_q(RowState<D>& st, const uint8_t* q4row, co
     }
   }
   }
+  if constexpr (OF) {
+    ofix_zero<D / 32>();
+  } else {
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) st.o[cb] = v16f{};
+    for (int cb = 0; cb < D / 32; ++cb) st.o[cb] = v16f{};
+  }
   st.m = -__builtin_inff();
   st.m_ref = -__builtin_inff();
   if constexpr (pv_of(PV) == PV_FP8) {

@@ -84,6 +84,10 @@ template <int D, bool COMP, int PV>
 __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) {
   using TL = TileLayout<D, PV>;
   constexpr int NB = kPrefillBuffers;  // LDS buffers per operand
+  // O^T in the fixed accumulation registers (attn_common.h, ofix_*): the
+  // method's kernel without the compensation, the one whose register budget
+  // leaves the compiler no reason to allocate accumulation registers itself
+  constexpr bool OF = !COMP && PV == PV_FP8;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar control flow
@@ -166,7 +170,7 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
   // while they are in flight
   for (int j = 0; j < NB - 1 && j < T; ++j) ld.issue_k(j, kbuf + j * TL::KREG, wave);
   for (int j = 0; j < NB - 2 && j < T; ++j) ld.issue_v(j, vbuf + j * TL::VREG, wave);
-  load_q<D, PV>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * TileLayout<D, PV>::KSB : nullptr,
+  load_q<D, PV, OF>(st, a.q4 ? a.q4 + qrow * (D / 2) : nullptr, a.q4 ? a.q4s + qrow * TileLayout<D, PV>::KSB : nullptr,
                 a.qbf ? a.qbf + qrow * D : nullptr, a.c2, rvalid, a.nv_gq, a.nv_gk);
   wait_vmem_le(0);
   __syncthreads();  // every wave's loads have landed before the scale patch
@@ -216,7 +220,7 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
     // (a wave's last P V also computes a product of whatever K buffer kb_cur
     // holds; that S is never used: one code path keeps the register budget)
     if (do_pv) {
-      pv_then_qk<D, PV, decltype(dma), SEED>(st, lo, vbuf + vb_prev * TL::VREG, pb, pscale, kbuf + kb_cur * TL::KREG,
+      pv_then_qk<D, PV, decltype(dma), SEED, OF>(st, lo, vbuf + vb_prev * TL::VREG, pb, pscale, kbuf + kb_cur * TL::KREG,
                                              s, init, dma);
     } else {
 #pragma unroll
@@ -240,14 +244,14 @@ __global__ void __launch_bounds__(512) k_prefill(AttnArgs a, int nwg_per_group) 
     if (t < Tw) {
       const float d32 = (COMP && !SEED) ? a.c2 * dl[(t & 31) * 32 + n] : 0.0f;
       const bool need_mask = (kTile * t + kTile - 1 > jmin_w) || (kTile * t + kTile > L);
-      softmax_tile<D, COMP && !SEED, PV>(st, s, t, need_mask, jlim, d32, pb, pscale);
+      softmax_tile<D, COMP && !SEED, PV, OF>(st, s, t, need_mask, jlim, d32, pb, pscale);
     }
     if (half == 0) end_window();
     kb_cur = kb_cur + 1 == NB ? 0 : kb_cur + 1;
     vb_prev = vb_prev + 1 == NB ? 0 : vb_prev + 1;
   }
 
-  if (rvalid) store_row<D, PV>(st, a.O + qrow * D, a.lse ? a.lse + qrow : nullptr);
+  if (rvalid) store_row<D, PV, OF>(st, a.O + qrow * D, a.lse ? a.lse + qrow : nullptr);
 }
 
 template <int D, int PV>
