@@ -397,12 +397,14 @@ def test_prefill_blockp_differs_where_blocks_spread():
     assert d > 0
 
 
-@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8, qfa.QFA_PV_FP8_BLOCKP, qfa.QFA_PV_FP4])
-def test_prefill_extreme_logits_far_and_rebase(pv):
+@pytest.mark.parametrize("pv,D", [(qfa.QFA_PV_FP8, 128), (qfa.QFA_PV_FP8, 64), (qfa.QFA_PV_FP8_BLOCKP, 128),
+                                  (qfa.QFA_PV_FP4, 128)])
+def test_prefill_extreme_logits_far_and_rebase(pv, D):
     """Logits far beyond 100 in log2 units (the kernel's subtract-first path)
     and a row max that climbs by more than 64 binades across the key range
-    (the frame rebase of O and l)."""
-    Skv, D = 1200, 128
+    (the frame rebase of O and l; for the method's format at both head
+    dimensions, whose kernels keep O in fixed accumulation registers)."""
+    Skv = 1200
     q, k, v = _rand_inputs(1, 2, 1, 64, Skv, D, seed=9, q_scale=30.0)
     k = (k.float() * (1.0 + torch.arange(Skv, device="cuda").float() / 200.0)[None, None, :, None]).to(torch.bfloat16)
     _check_prefill(q, k, v, False, 1.0 / math.sqrt(D), False, _all_rows(1, 2, 64), "extreme-logits", fused=True,
