@@ -107,6 +107,33 @@ def test_append_matches_oracle_and_feeds_decode():
     assert torch.equal(O1, O2) and torch.equal(l1, l2)
 
 
+def test_append_order_sensitive_kbar_matches_oracle():
+    """Appends in chunks that split a K-bar tile whose channel sums binary64
+    does not add exactly (values 2^60 apart): after every append the cache's
+    K-bar must still be the oracle's token-order sum over the tile's present
+    rows, and the K codes must match the oracle's quantiser bit for bit."""
+    B, Hkv, S, D = 1, 2, 300, 128
+    k, v = _data(B, Hkv, S, D, seed=21)
+    kf = k.float()
+    kf[0, 0, :, 0] = 1.0
+    kf[0, 0, 3, 0], kf[0, 0, 90, 0] = 2.0 ** 60, -(2.0 ** 60)     # tile 0: the sum restarts at token 90
+    kf[0, 1, 140, 5], kf[0, 1, 200, 5] = -(2.0 ** 70), 2.0 ** 70  # tile 1, the other KV head
+    k = kf.to(torch.bfloat16)
+    c = qfa.kv_cache(B, Hkv, S, D, smooth=True)
+    L = 0
+    for n in (60, 45, 60, 1, 100, 34):
+        say("kv_append order-sensitive K-bar, at", L, "n", n)
+        kl = torch.tensor([L], dtype=torch.int32, device="cuda")
+        qfa.kv_append(c, k[:, :, L:L + n].contiguous(), v[:, :, L:L + n].contiguous(), kv_lens=kl)
+        torch.cuda.synchronize()
+        L += n
+        oc, os_, ok = oracle.quantize_qk4(bf16_bits(k[:, :, :L]), smooth=True)
+        nt = (L + 127) // 128
+        assert np.array_equal(to_np(c["kbar"][:, :, :nt].view(torch.int16)).view(np.uint16), ok), ("K-bar", L)
+        assert np.array_equal(to_np(c["k4"][:, :, :L]), oc), ("K codes", L)
+        assert np.array_equal(to_np(c["k4s"][:, :, :L]), os_), ("K scales", L)
+
+
 def _check_formats_one_shot(c, k, v, lens, smooth, pv, g, label):
     for b, L in enumerate(lens):
         if L == 0:
