@@ -20,7 +20,8 @@ FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
-SYMBOLS = ("probe_cvt", "probe_s_tile", "probe_s_tile_seeded", "probe_tile_rowsum", "probe_delta", "probe_lds_fill")
+SYMBOLS = ("probe_cvt", "probe_s_tile", "probe_s_tile_seeded", "probe_tile_rowsum", "probe_delta", "probe_exp2",
+           "probe_lds_fill")
 
 
 def build(verbose: bool = False) -> str:
@@ -54,6 +55,8 @@ def load():
     L.probe_tile_rowsum.argtypes = [P, P, P, P]
     L.probe_delta.restype = I
     L.probe_delta.argtypes = [P, I, I, P, I, I, I, P]
+    L.probe_exp2.restype = I
+    L.probe_exp2.argtypes = [P, ctypes.c_long, P]
     L.probe_lds_fill.restype = I
     L.probe_lds_fill.argtypes = [ctypes.c_uint32, I, I]
     return L

@@ -23,6 +23,7 @@
 //  - probe_delta: the rank-one compensation term of 32 tiles x 32 query rows
 //    (compute_delta: K-bar . Q_bf16 on the FP64 MFMA), written out as the
 //    LDS slab the kernels read, dl[tile][row].
+//  - probe_exp2: v_exp_f32 (the kernels' exponential) applied to an array.
 //  - probe_lds_fill: fills the LDS of every compute unit with a byte pattern
 //    (a regression check that no kernel reads LDS bytes it did not write).
 //
@@ -97,6 +98,11 @@ __global__ void __launch_bounds__(64) k_s_tile(const uint8_t* q4, const uint8_t*
       const int key = score_key<PV_FP8>(c, g, rr);
       if (key < nk) S[n * kTile + key] = s[c][rr];
     }
+}
+
+__global__ void k_exp2(const float* __restrict__ x, long n, float* __restrict__ out) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) out[i] = __builtin_amdgcn_exp2f(x[i]);
 }
 
 __global__ void __launch_bounds__(256) k_lds_fill(uint32_t pattern, int words) {
@@ -186,6 +192,13 @@ int probe_delta(const uint16_t* kbar, int tlim, int tau0, const uint16_t* q, int
     hipLaunchKernelGGL(k_delta<128>, dim3(1), dim3(64), 0, 0, kbar, tlim, tau0, q, q_stride, nrows, out);
   else
     return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int probe_exp2(const float* x, long n, float* out) {
+  if (n <= 0) return (int)hipErrorInvalidValue;
+  const int blocks = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
+  hipLaunchKernelGGL(k_exp2, dim3(blocks), dim3(256), 0, 0, x, n, out);
   return (int)hipGetLastError();
 }
 
