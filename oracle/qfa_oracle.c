@@ -63,11 +63,13 @@
  *    j <= i + (L - Sq).  Query head h reads kv head h / (Hq / Hkv).
  *  - Decode splits are contiguous runs of whole 128-token tiles, merged by
  *    log-sum-exp.
- *  - The exponent argument of P (which decides an integer code) is formed in
- *    binary32 as the kernel forms it (fp32_arg = 1):
+ *  - The exponent argument of P and its exponential (which decide an integer
+ *    code) are binary32, the precision the kernels decide in (fp32_arg = 1):
  *    y = fl32(fl32(S) + fl32(c2 * fl32(delta))), m' = max(m, ceil(max y)),
- *    P = E4M3(256 * 2^(y - m')).  Without the compensation y = S exactly.
- *    Every exponential, sum and product is still evaluated in binary64.
+ *    P = E4M3(256 * fl32(2^(y - m'))) with fl32 the correctly rounded binary32
+ *    value (ties of the E4M3 rounding go to the even code).  Without the
+ *    compensation y = S exactly.  Every other exponential, sum and product is
+ *    evaluated in binary64.
  *  - Contrast cases (not the method; see tile_p): P in E4M3 with one E8M0
  *    scale per (row, 32 keys) instead of one per row, and MXFP4 P and V
  *    ("QK4PV4": E2M1 codes, one E8M0 scale per 32 keys of a row for P and per
@@ -527,14 +529,24 @@ void orc_attn_exact_rows(const double* Q, const int64_t* qpos, int64_t n, const 
 #define QFA_P_E4M3_BLOCK 2
 #define QFA_P_E2M1_BLOCK 3
 #define QFA_P_BLOCK_FLOOR 64.0
-static void tile_p(const double* y, int64_t n, double mnew, int p_mode, double* P) {
+/* 2^x, rounded to binary32 when the exponential is taken in binary32 (exp32):
+ * the P code is an integer decided by floating point, and the kernels decide
+ * it from a binary32 exponential.  exp2 in binary64 is far more accurate than
+ * half a binary32 ulp, so the cast gives the correctly rounded binary32 value
+ * (up to double rounding within 2^-53 of a binary32 midpoint). */
+static double pexp2(double x, int exp32) {
+  double e = exp2(x);
+  return exp32 ? (double)(float)e : e;
+}
+
+static void tile_p(const double* y, int64_t n, double mnew, int p_mode, int exp32, double* P) {
   if (p_mode == QFA_P_EXACT || p_mode == QFA_P_E4M3) {
     for (int64_t j = 0; j < n; ++j) {
       if (y[j] == -INFINITY) {
         P[j] = 0.0;
         continue;
       }
-      double p = ldexp(exp2(y[j] - mnew), 8);
+      double p = ldexp(pexp2(y[j] - mnew, exp32 && p_mode == QFA_P_E4M3), 8);
       P[j] = p_mode == QFA_P_E4M3 ? orc_e4m3_value(orc_e4m3_encode(p)) : p;
     }
     return;
@@ -553,9 +565,9 @@ static void tile_p(const double* y, int64_t n, double mnew, int p_mode, double* 
       }
       double v;
       if (p_mode == QFA_P_E4M3_BLOCK)
-        v = orc_e4m3_value(orc_e4m3_encode(ldexp(exp2(y[j] - e), 8)));
+        v = orc_e4m3_value(orc_e4m3_encode(ldexp(pexp2(y[j] - e, exp32), 8)));
       else
-        v = orc_e2m1_value(orc_e2m1_encode(ldexp(exp2(y[j] - e), 2)));
+        v = orc_e2m1_value(orc_e2m1_encode(ldexp(pexp2(y[j] - e, exp32), 2)));
       P[j] = ldexp(v, (int)(e - mnew));
     }
   }
@@ -618,7 +630,7 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
     const double mt = ceil(ymax);
     const double mnew = (m == -INFINITY || mt > m) ? mt : m;
     const double alpha = (m == -INFINITY) ? 0.0 : exp2(m - mnew);
-    tile_p(S, j1 - j0, mnew, p_mode, P);
+    tile_p(S, j1 - j0, mnew, p_mode, fp32_arg, P);
     /* running sum of the same (decoded) P values that multiply V, and output
      * rescale  [FA4tut "Direct-P"; "注意力慢在哪儿"] */
     double lt = 0.0;
@@ -650,7 +662,8 @@ static int split_row(const double* q, const double* qc, int64_t i, const double*
  *   p_mode      how P is quantised: QFA_P_EXACT (0, identity), QFA_P_E4M3
  *               (1, the method), QFA_P_E4M3_BLOCK (2), QFA_P_E2M1_BLOCK (3);
  *               see tile_p
- *   fp32_arg    1: exponent argument formed in binary32 (see split_row);
+ *   fp32_arg    1: exponent argument and the exponential of quantised P
+ *                  in binary32 (see split_row, tile_p);
  *               0: everything in binary64
  * Outputs O [n][D], lse [n].  Rows with no visible key get O = 0, lse = -inf.
  */

@@ -6,15 +6,17 @@ code of each probability and the integer running max), the oracle and the
 kernels decide in binary32: the argument of P is
     y = fl32( fl32(S') + fl32( c2 * fl32(delta) ) ),   c2 = fl32(scale * fl32(log2 e)),
 the running max m' = max(m, ceil(max_j y_j)) per 128-key tile, and
-P = E4M3(256 * 2^(y - m')) (the online softmax of the FP4 tutorial's section
-"注意力慢在哪儿", with the rank-one compensation term of the MpFA abstract).
-The brute force below rebuilds that row computation with numpy float32
-arithmetic (each operation rounds to binary32) and a nearest-value E4M3
-rounding over torch's float8 decode table, independent of the oracle's C
-code.  The inputs are built so that the binary32 and binary64 arguments give
-different P codes, and so that a plausible mistake in the rounding order --
+P = E4M3(256 * fl32(2^(y - m'))), the exponential also rounded to binary32
+(the online softmax of the FP4 tutorial's section "注意力慢在哪儿", with the
+rank-one compensation term of the MpFA abstract).  The brute force below
+rebuilds that row computation with numpy float32 arithmetic (each operation
+rounds to binary32) and a nearest-value E4M3 rounding over torch's float8
+decode table (ties to the even code), independent of the oracle's C code.
+The inputs are built so that the binary32 and binary64 arguments give
+different P codes, so that a plausible mistake in the rounding order --
 rounding c2 * delta in binary64 first, or adding delta before rounding S' --
-gives different codes too: the test tells all of these apart.
+gives different codes too, and so that a binary64 exponential of the binary32
+argument does as well: the test tells all of these apart.
 
 Dequantisers.  Known codes at known positions are decoded with the E2M1
 magnitudes printed in the tutorial's section "FP4 只有约 15 个可表示的数"
@@ -47,13 +49,24 @@ E4M3_POS = _e4m3_table()
 
 def e4m3_nearest(x):
     """E4M3 rounding of non-negative x by nearest-value search over torch's
-    decode table (ties do not occur for these inputs; asserted)."""
+    decode table; an exact tie goes to the even code (the table index is the
+    code)."""
     x = np.asarray(x, np.float64)
     d = np.abs(x[..., None] - E4M3_POS)
-    i = np.argmin(d, axis=-1)
+    i = np.argmin(d, axis=-1)               # the lower of two tied codes
     srt = np.sort(d, axis=-1)
-    assert np.all((srt[..., 1] - srt[..., 0] > 0) | (x == 0)), "tie in E4M3 rounding"
+    tie = (srt[..., 1] == srt[..., 0]) & (x != 0)
+    i = np.where(tie & (i % 2 == 1), i + 1, i)
     return E4M3_POS[i]
+
+
+def p_codes(y, mnew, mode):
+    """E4M3(256 * 2^(y - m')): the exponential rounded to binary32, except in
+    the all-binary64 mode and the binary64-exponential mistake."""
+    e = np.exp2(y - mnew)
+    if mode not in ("fp64", "exp64"):
+        e = e.astype(np.float32).astype(np.float64)
+    return e4m3_nearest(256.0 * e)
 
 
 def argument(Sp, delta, scale, mode):
@@ -71,6 +84,8 @@ def argument(Sp, delta, scale, mode):
         return (Sp.astype(np.float32) + d32).astype(np.float64)
     if mode == "add_first":       # mistake: S' + c2 delta added before any rounding
         return (Sp + float(c2f) * float(np.float32(delta))).astype(np.float32).astype(np.float64)
+    if mode == "exp64":           # mistake: the binary32 argument, but a binary64 exponential
+        return argument(Sp, delta, scale, "fp32")
     raise ValueError(mode)
 
 
@@ -86,12 +101,15 @@ def bruteforce_row(Sp, deltas, V, scale, mode, tile=128):
         y = argument(Sp[j0:j1], deltas[t], scale, mode)
         mnew = max(m, math.ceil(float(y.max())))
         alpha = 0.0 if m == -math.inf else 2.0 ** (m - mnew)
-        P = e4m3_nearest(256.0 * np.exp2(y - mnew))
+        P = p_codes(y, mnew, mode)
         codes.append(P * 2.0 ** (mnew - 0.0))
         l = alpha * l + P.sum()
         o = alpha * o + P @ V[j0:j1]
         m = mnew
     return o / l, math.log(2.0) * (m + math.log2(l / 256.0)), np.concatenate(codes)
+
+
+MODES = ("fp32", "fp64", "c2_in_fp64", "add_first", "exp64")
 
 
 def _case(seed, scale):
@@ -119,11 +137,11 @@ def _case(seed, scale):
         tgt[1:] = 1.0 + np.log2(rng.choice(mids, 127) / 256.0)
         Sp[128:256] = tgt - c2d * d1
         Sp[128:256] = Sp[128:256].astype(np.float32).astype(np.float64) + rng.uniform(-1, 1, 128) * 2.0**-40
-        ys = {m: argument(Sp[128:256], d1, scale, m) for m in ("fp32", "fp64", "c2_in_fp64", "add_first")}
+        ys = {m: argument(Sp[128:256], d1, scale, m) for m in MODES}
         if any(math.ceil(y.max()) != 1 for y in ys.values()):
             continue
-        pc = {m: e4m3_nearest(256.0 * np.exp2(y - 1.0)) for m, y in ys.items()}
-        if all(np.any(pc["fp32"] != pc[m]) for m in ("fp64", "c2_in_fp64", "add_first")):
+        pc = {m: p_codes(y, 1.0, m) for m, y in ys.items()}
+        if all(np.any(pc["fp32"] != pc[m]) for m in MODES[1:]):
             break
     else:
         raise AssertionError("no discriminating input found")
@@ -144,7 +162,7 @@ def test_binary32_argument_matches_float32_bruteforce(seed):
                                     fp32_arg=True)
     Ob, lb = oracle.attn_quant_rows(Q, np.zeros(1, np.int64), K, V, 1, False, scale, Qc=Q, Kbar=Kbar,
                                     fp32_arg=False)
-    res = {m: bruteforce_row(Sp, deltas, V, scale, m) for m in ("fp32", "fp64", "c2_in_fp64", "add_first")}
+    res = {m: bruteforce_row(Sp, deltas, V, scale, m) for m in MODES}
     # the oracle's binary32 path is the float32 brute force, to rounding of the binary64 sums
     assert np.abs(Oa[0] - res["fp32"][0]).max() < 1e-12
     assert abs(la[0] - res["fp32"][1]) < 1e-12
@@ -152,7 +170,7 @@ def test_binary32_argument_matches_float32_bruteforce(seed):
     assert np.abs(Ob[0] - res["fp64"][0]).max() < 1e-12
     assert abs(lb[0] - res["fp64"][1]) < 1e-12
     # and the inputs discriminate: every other rounding order gives other codes and another O
-    for m in ("fp64", "c2_in_fp64", "add_first"):
+    for m in MODES[1:]:
         assert np.any(res[m][2] != res["fp32"][2]), m
         assert np.abs(res[m][0] - Oa[0]).max() > 1e-9, m
 
