@@ -397,3 +397,26 @@ def test_decode_after_lds_filled_with_nan_codes(probe, D, lens):
                              exact=False)
     compare_o(Og[rows[:, 0], rows[:, 1]], res["O_q"], to_np(lse)[rows[:, 0], rows[:, 1]], res["lse_q"],
               label="decode-after-lds-fill-D%d" % D)
+
+
+@pytest.mark.parametrize("lo,hi", [(-1.0, 1.0), (-30.0, 30.0), (-120.0, 120.0)])
+def test_exp2_within_one_ulp_of_correctly_rounded(probe, lo, hi):
+    """The kernels' exponential (v_exp_f32) against the correctly rounded
+    binary32 2^x, over the arguments the softmax sees: at most one ulp off.
+    The oracle decides P codes from the correctly rounded binary32 value, so
+    the two decisions can differ only where 256 * 2^(y - m') lies within that
+    ulp of an E4M3 rounding midpoint."""
+    rng = np.random.default_rng(int(hi))
+    n = 1 << 20
+    x = rng.uniform(lo, hi, n).astype(np.float32)
+    xt = torch.from_numpy(x).cuda()
+    out = torch.empty_like(xt)
+    say("exp2 probe [%g, %g], %d arguments" % (lo, hi, n))
+    assert probe.probe_exp2(xt.data_ptr(), n, out.data_ptr()) == 0
+    torch.cuda.synchronize()
+    g = to_np(out)
+    cr = np.exp2(x.astype(np.float64)).astype(np.float32)
+    ok = np.isfinite(cr) & (cr >= np.float32(2.0 ** -126))          # normal results
+    ulp = g[ok].view(np.int32).astype(np.int64) - cr[ok].view(np.int32).astype(np.int64)
+    say("exp2 probe: %.2f%% one ulp off, max %d" % (100.0 * np.mean(ulp != 0), int(np.abs(ulp).max())))
+    assert int(np.abs(ulp).max()) <= 1
