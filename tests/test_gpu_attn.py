@@ -278,6 +278,18 @@ def test_prefill_random_shapes(i):
     _check_prefill(q, k, v, causal, 1.0 / math.sqrt(D), smooth, _all_rows(B, Hq, Sq), label, fused=fused)
 
 
+@pytest.mark.parametrize("i", range(200, 216))
+def test_prefill_random_compensated(i):
+    """The random-shape recipe with the compensation forced on (K with a
+    per-channel offset): the compensated exponent argument has a full binary32
+    mantissa, so these rows are where P codes near E4M3 rounding boundaries
+    are decided (both sides from a binary32 exponential)."""
+    B, Hq, Hkv, Sq, Skv, D, causal, _, fused, _, qs = _random_prefill_case(i)
+    label = "crand%d B%d H%d/%d S%d/%d D%d causal%d fused%d" % (i, B, Hq, Hkv, Sq, Skv, D, causal, fused)
+    q, k, v = _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed=2000 + i, k_offset=3.0, q_scale=qs)
+    _check_prefill(q, k, v, causal, 1.0 / math.sqrt(D), True, _all_rows(B, Hq, Sq), label, fused=fused)
+
+
 @pytest.mark.parametrize("i", range(8))
 def test_decode_random_shapes(i):
     """Seeded random decode shape: batch, GQA ratio (up to 40 query heads per KV
