@@ -269,7 +269,7 @@ def _random_prefill_case(i):
     return B, Hkv * G, Hkv, Sq, Skv, D, causal, smooth, fused, koff, qs
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(64))
 def test_prefill_random_shapes(i):
     B, Hq, Hkv, Sq, Skv, D, causal, smooth, fused, koff, qs = _random_prefill_case(i)
     label = "rand%d B%d H%d/%d S%d/%d D%d causal%d comp%d fused%d" % (i, B, Hq, Hkv, Sq, Skv, D, causal, smooth,
@@ -290,7 +290,7 @@ def test_prefill_random_compensated(i):
     _check_prefill(q, k, v, causal, 1.0 / math.sqrt(D), True, _all_rows(B, Hq, Sq), label, fused=fused)
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(24))
 def test_decode_random_shapes(i):
     """Seeded random decode shape: batch, GQA ratio (up to 40 query heads per KV
     head, i.e. two row chunks), ragged cache lengths including empty ones, split
