@@ -497,6 +497,27 @@ def test_prefill_nvfp4_small_all_rows(case):
     _check_prefill_nv(q, k, v, causal, 1.0 / math.sqrt(D), smooth, _all_rows(B, Hq, Sq), label)
 
 
+@pytest.mark.parametrize("fmt", ["blockp", "fp4", "nvfp4"])
+@pytest.mark.parametrize("i", range(400, 416))
+def test_prefill_formats_random_shapes(i, fmt):
+    """The random-shape recipe in the contrast formats: block-scaled E4M3 P
+    with the compensation as drawn; MXFP4 P/V and NVFP4 Q/K without it (where
+    the compensated form of those two can move a P code across a rounding
+    boundary on the last bit of the exponential, which an E2M1 step or the
+    add-after-products order makes large enough to exceed a bar)."""
+    B, Hq, Hkv, Sq, Skv, D, causal, smooth, fused, koff, qs = _random_prefill_case(i)
+    if fmt != "blockp":
+        smooth = False
+    label = "%s-rand%d B%d H%d/%d S%d/%d D%d causal%d comp%d fused%d" % (fmt, i, B, Hq, Hkv, Sq, Skv, D, causal,
+                                                                       smooth, fused)
+    q, k, v = _rand_inputs(B, Hq, Hkv, Sq, Skv, D, seed=2000 + i, k_offset=koff, q_scale=qs)
+    if fmt == "nvfp4":
+        _check_prefill_nv(q, k, v, causal, 1.0 / math.sqrt(D), smooth, _all_rows(B, Hq, Sq), label)
+    else:
+        pv = qfa.QFA_PV_FP8_BLOCKP if fmt == "blockp" else qfa.QFA_PV_FP4
+        _check_prefill(q, k, v, causal, 1.0 / math.sqrt(D), smooth, _all_rows(B, Hq, Sq), label, fused=fused, pv=pv)
+
+
 def test_decode_nvfp4_varlen():
     B, Hq, Hkv, Smax, D = 3, 8, 2, 1000, 128
     q, k, v = _rand_inputs(B, Hq, Hkv, 1, Smax, D, seed=25, q_scale=2.0)
