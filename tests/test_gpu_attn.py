@@ -310,6 +310,26 @@ def test_decode_random_shapes(i):
     _check_decode(q, k, v, splits, kv_lens=lens, label=label, smooth=smooth)
 
 
+@pytest.mark.parametrize("pv", [qfa.QFA_PV_FP8_BLOCKP, qfa.QFA_PV_FP4], ids=["blockp", "fp4"])
+@pytest.mark.parametrize("i", range(100, 116))
+def test_decode_formats_random_shapes(i, pv):
+    """The random decode recipe in the P/V contrast formats (block-scaled E4M3
+    P with the compensation as drawn, MXFP4 P/V without it)."""
+    rng = np.random.default_rng(3000 + i)
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 4, 8, 40]))
+    B = int(rng.integers(1, 5))
+    Smax = int(rng.integers(1, 5000))
+    lens = [int(x) for x in rng.integers(0, Smax + 1, size=B)]
+    lens[0] = Smax
+    splits = int(rng.choice([0, 1, 2, 5, 16]))
+    smooth = bool(rng.integers(2)) and pv == qfa.QFA_PV_FP8_BLOCKP
+    label = "drand%d-pv%d B%d H%d/%d S%d D%d splits%d comp%d" % (i, pv, B, Hkv * G, Hkv, Smax, D, splits, smooth)
+    q, k, v = _rand_inputs(B, Hkv * G, Hkv, 1, Smax, D, seed=4000 + i, k_offset=3.0 if smooth else 0.0)
+    _check_decode(q, k, v, splits, kv_lens=lens, label=label, smooth=smooth, pv=pv)
+
+
 @pytest.mark.parametrize("splits", [3, 0, 1])
 def test_decode_small_varlen(splits):
     q, k, v = _rand_inputs(3, 8, 2, 1, 1000, 128, seed=11, q_scale=2.0)
